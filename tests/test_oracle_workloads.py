@@ -1,0 +1,55 @@
+"""The oracle on the seeded workloads: generator determinism and planted-needle recovery."""
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import block
+
+
+def test_generator_is_deterministic_and_subsettable():
+    a = synth.decode_case(2, L=4096, B=3)
+    b = synth.decode_case(2, L=4096, B=3)
+    for key in ("q_full", "k", "v"):
+        assert np.array_equal(a[key], b[key])
+    one = synth.decode_case(2, L=4096, B=3, seqs=[2])
+    assert np.array_equal(one["k"], a["k"][2 * 4096:3 * 4096])
+    assert np.array_equal(one["q_full"][0], a["q_full"][2])
+    assert a["needles"][2] == one["needles"][0]
+
+
+def test_ragged_lengths_in_range():
+    lens = synth.ragged_lengths(5)
+    assert lens.shape == (8,) and lens.min() >= 65536 and lens.max() <= 524288
+    assert np.array_equal(lens, synth.ragged_lengths(5))
+
+
+def _seq_values(case, i):
+    L = int(case["lengths"][i])
+    r0 = int(case["row_start"][i])
+    kv = case["spec"]["kv"]
+    k = block.cache_values(case["k"][r0:r0 + L], kv if kv != "e4m3" else "f32")
+    v = block.cache_values(case["v"][r0:r0 + L], kv if kv != "e4m3" else "f32")
+    qt = case["spec"]["q"]
+    q = block.cache_values(case["q_full"][i], qt)
+    return q, k, v
+
+
+def test_config1_needles_recovered_full_size():
+    case = synth.decode_case(1)
+    q, k, v = _seq_values(case, 0)
+    out = block.full_layer(q, k, v, synth.TOP_K, synth.WINDOW)
+    assert np.all(out["cnt"] == 1152)
+    for (p, t, h) in case["needles"][0]:
+        assert p in set(out["idx"][t, 0, :1152].tolist()), (p, t, h)
+
+
+@pytest.mark.slow
+def test_config2_needles_recovered_one_sequence():
+    case = synth.decode_case(2, seqs=[5])
+    q, k, v = _seq_values(case, 0)
+    out = block.full_layer(q, k, v, synth.TOP_K, synth.WINDOW)
+    sel = set(out["idx"][0, 0, :1152].tolist())
+    assert len(case["needles"][0]) == 64
+    for (p, t, h) in case["needles"][0]:
+        assert p in sel
