@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Hybrid-block decode benchmark of libhysparse on one MI355X.
+
+A step is one pass of the whole hot path over one batch: the full-attention
+layer with token selection (hs_full_attn_select) followed by the block's sparse
+layers (hs_sparse_attn, each with its own queries, reusing the cache and the
+indices).  Default workload: 32 sequences x 131072 cached rows, bf16 MQA cache,
+32 query heads, 1 full + 5 sparse layers (the 128K decode configuration).
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+  value        queries/s = B * n_q / median step time (HIP events, inputs resident in HBM)
+  roofline     the dominant kernel's algorithmic bytes / its average launch time,
+               measured with HIP events on the library's stream over a timed region
+  cpu_baseline the float64 CPU oracle timed on this host on a bounded sample
+"""
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "hybrid-block decode queries/s + achieved HBM GB/s at 128K–1M ctx, 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 5],
+                    help="2: 32 x 128K bf16 (default); 5: ragged 8 x 64K-512K, 4 blocks")
+    ap.add_argument("--L", type=int, default=None, help="context length override (sweeps)")
+    ap.add_argument("--B", type=int, default=None, help="batch override (sweeps)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle time budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true", help="skip the Infinity Cache flush between steps")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); the hybrid-block "
+              "path has no multi-GPU mode in this build (independent sequences would shard as pure data "
+              "parallelism with no exchange)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synth
+    from long_context_split_amd import hysparse as hs
+
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    spec = dict(synth.CONFIGS[args.config])
+    n_blocks = spec.get("n_blocks", 1)
+    top_k, window = synth.TOP_K, synth.WINDOW
+
+    # ---------------------------------------------------------------- inputs (seeded, synthetic)
+    t0 = time.time()
+    blocks = []
+    for blk in range(n_blocks):
+        case = synth.decode_case(args.config, L=args.L, B=args.B, block=blk)
+        k = torch.from_numpy(case["k"].view(np.int16)).to(dev).view(torch.bfloat16)
+        v = torch.from_numpy(case["v"].view(np.int16)).to(dev).view(torch.bfloat16)
+        kv = hs.KVCache(k, v, case["lengths"], case["row_start"])
+        qf = torch.from_numpy(case["q_full"].view(np.int16)).to(dev).view(torch.bfloat16)
+        qs = [torch.from_numpy(q.view(np.int16)).to(dev).view(torch.bfloat16) for q in case["q_sparse"]]
+        blocks.append(dict(case=case, kv=kv, qf=qf, qs=qs))
+        log(f"block {blk}: generated and uploaded B={len(case['lengths'])} "
+            f"L={int(case['lengths'].min())}..{int(case['lengths'].max())} ({time.time() - t0:.1f}s)")
+    lens = blocks[0]["case"]["lengths"]
+    B = len(lens)
+    n_q, H = spec["n_q"], spec["H"]
+    n_sparse = spec["n_sparse"]
+
+    # outputs and workspaces, allocated once
+    for bl in blocks:
+        kv = bl["kv"]
+        p = hs.params(H, n_q, top_k, window)
+        bl["out"] = torch.empty((B, n_q, H, 128), dtype=torch.float32, device=dev)
+        bl["lse"] = torch.empty((B, n_q, H), dtype=torch.float32, device=dev)
+        bl["idx"] = torch.empty((B, n_q, 1, top_k + window), dtype=torch.int32, device=dev)
+        bl["cnt"] = torch.empty((B, n_q, 1), dtype=torch.int32, device=dev)
+        bl["ws_full"] = hs.workspace(hs.full_attn_select_workspace_size(kv, p), dev)
+        bl["ws_sp"] = hs.workspace(hs.sparse_attn_workspace_size(kv, p), dev)
+        bl["so"] = [torch.empty((B, n_q, H, 128), dtype=torch.float32, device=dev) for _ in range(n_sparse)]
+
+    def step():
+        for bl in blocks:
+            kv = bl["kv"]
+            hs.full_attn_select(kv, bl["qf"], top_k, window, out=bl["out"], lse=bl["lse"], sel_idx=bl["idx"],
+                                sel_count=bl["cnt"], ws=bl["ws_full"])
+            for i in range(n_sparse):
+                hs.sparse_attn(kv, bl["qs"][i], bl["idx"], bl["cnt"], top_k, window, out=bl["so"][i],
+                               ws=bl["ws_sp"])
+
+    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    # ---------------------------------------------------------------- warmup
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    # ---------------------------------------------------------------- timed region: step time
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.time()
+    for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)                 # evict the 256 MB Infinity Cache between steps
+        ev[i][0].record()
+        step()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.time() - wall0
+    times = sorted(a.elapsed_time(b) for a, b in ev)
+    ms = statistics.median(times)
+    p10 = times[int(0.1 * (len(times) - 1))]
+    p90 = times[int(0.9 * (len(times) - 1))]
+    log(f"timed {args.steps} steps: median {ms:.4f} ms (p10 {p10:.4f}, p90 {p90:.4f}), wall {wall:.2f}s")
+
+    # ---------------------------------------------------------------- timed region: per-kernel events
+    hs.timing_enable(True)
+    hs.timing_collect()
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        step()
+    torch.cuda.synchronize()
+    recs = hs.timing_collect()
+    hs.timing_enable(False)
+    per = {}
+    for name, t in recs:
+        per.setdefault(name, []).append(t)
+    kern = {n: dict(launches=len(v), avg_ms=sum(v) / len(v), total_ms_per_step=sum(v) / args.steps)
+            for n, v in per.items()}
+    for n, d in sorted(kern.items(), key=lambda x: -x[1]["total_ms_per_step"]):
+        log(f"kernel {n:22s} launches/step {d['launches'] / args.steps:4.1f} avg {d['avg_ms'] * 1e3:9.2f} us "
+            f"per step {d['total_ms_per_step'] * 1e3:9.2f} us")
+
+    # ---------------------------------------------------------------- algorithmic bytes
+    row_bytes = 2 * 128 * 2                                     # bf16 K + V row
+    sum_L = int(sum(int(x) for x in lens))
+    union_rows = 0
+    for bl in blocks:
+        cnt = bl["cnt"].cpu().numpy()
+        union_rows += int(cnt.max(axis=1).sum()) if n_q == 1 else int(cnt.sum())
+    q_bytes = n_blocks * (1 + n_sparse) * B * n_q * H * 128 * 2
+    o_bytes = n_blocks * (1 + n_sparse) * B * n_q * H * 128 * 4
+    idx_bytes = n_blocks * (1 + n_sparse) * B * n_q * (top_k + window) * 4
+    alg_bytes = n_blocks * sum_L * row_bytes + n_sparse * union_rows * row_bytes + q_bytes + o_bytes + idx_bytes
+    eff_gbps = alg_bytes / (ms * 1e-3) / 1e9
+    queries = B * n_q
+    qps = queries / (ms * 1e-3)
+
+    dom = max(kern.items(), key=lambda x: x[1]["total_ms_per_step"])[0] if kern else None
+    k1 = kern.get("attn_partial_dense")
+    k1_bytes = sum_L * row_bytes                                 # per launch (one block's full layer)
+    roof = None
+    if k1:
+        ach = k1_bytes / (k1["avg_ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "attn_partial_dense",
+                "algorithmic_bytes_per_launch": k1_bytes, "avg_launch_us": round(k1["avg_ms"] * 1e3, 2),
+                "dominant_kernel_by_time": dom}
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(blocks[0]["case"], top_k, window, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(qps, 2),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": spec["name"] if args.L is None and args.B is None else
+            f"{spec['name']}_L{args.L or 'cfg'}_B{args.B or 'cfg'}",
+            "batch": B, "seq_len": int(lens.max()) if args.config == 2 else [int(x) for x in lens],
+            "query_heads": H, "kv_heads": 1, "head_dim": 128, "q_tokens": n_q, "top_k": top_k, "window": window,
+            "sparse_layers": n_sparse, "blocks": n_blocks, "kv_dtype": "bf16",
+        },
+        "achieved_hbm_GBps": round(eff_gbps, 1),
+        "hbm_frac": round(eff_gbps / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_step": alg_bytes,
+        "ms_p10": round(p10, 5), "ms_p90": round(p90, 5),
+        "kernels": {n: {"launches_per_step": d["launches"] / args.steps, "avg_us": round(d["avg_ms"] * 1e3, 2)}
+                    for n, d in kern.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "timing": "HIP events per step; Infinity Cache flushed between steps" if flush is not None
+        else "HIP events per step; no cache flush",
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(case, top_k, window, budget_s):
+    """The float64 oracle, as it stands, on sequences of the same workload until the budget is spent."""
+    import numpy as np
+    from oracle import attention, block
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = None
+    cores = len(os.sched_getaffinity(0))
+    lens, starts = case["lengths"], case["row_start"]
+    t0 = time.time()
+    done = 0
+    for i in range(len(lens)):
+        L, r0 = int(lens[i]), int(starts[i])
+        k = block.cache_values(case["k"][r0:r0 + L], "bf16")
+        v = block.cache_values(case["v"][r0:r0 + L], "bf16")
+        q = block.cache_values(case["q_full"][i], "bf16")
+        out = block.full_layer(q, k, v, top_k, window)
+        for qs in case["q_sparse"]:
+            attention.sparse_attention(block.cache_values(qs[i], "bf16"), k, v, out["idx"], out["cnt"])
+        done += 1
+        if time.time() - t0 >= budget_s:
+            break
+    el = time.time() - t0
+    n_q = case["q_full"].shape[1]
+    log(f"cpu oracle: {done} sequences in {el:.2f}s")
+    return {"value": round(done * n_q / el, 3), "unit": "queries/s", "cores": blas_threads or cores,
+            "host_cores_visible": cores, "kind": "oracle",
+            "sample": f"{done} of {len(lens)} sequences of the same step (full layer + select + "
+                      f"{len(case['q_sparse'])} sparse layers each), float64 NumPy", "seconds": round(el, 2)}
+
+
+if __name__ == "__main__":
+    main()

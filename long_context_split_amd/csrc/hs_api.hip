@@ -1,0 +1,462 @@
+// libhysparse C ABI: argument validation, workspace planning and kernel launches.
+// Every check runs before anything is enqueued; on an error nothing is launched
+// and no output or workspace byte is written.  The library never synchronises
+// and never allocates device memory.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "hysparse.h"
+#include "hs_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hs_status fail(hs_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+hs_status fail(hs_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+hs_status hip_fail(hipError_t e, const char* what) {
+  return fail(HS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------- optional kernel timing
+
+std::mutex g_tmu;
+bool g_timing = false;
+struct TimeRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+std::vector<TimeRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t pool_get() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs one launch; when timing is on, brackets it with events on its stream.
+template <class F>
+hipError_t timed(const char* name, hipStream_t s, F&& launch) {
+  if (!g_timing) return launch();
+  std::lock_guard<std::mutex> lk(g_tmu);
+  hipEvent_t a = pool_get(), b = pool_get();
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, s);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, s);
+  g_recs.push_back({name, a, b});
+  return e;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int env_int(const char* name, int dflt) {
+  const char* s = getenv(name);
+  if (!s || !*s) return dflt;
+  return atoi(s);
+}
+
+// ---------------------------------------------------------------- shared validation
+
+struct CacheInfo {
+  int B, n_kv, maxL;
+  int64_t total;
+};
+
+hs_status check_cache(const hs_kv_cache* kv, CacheInfo& ci, bool need_rows) {
+  if (!kv) return fail(HS_ERR_INVALID_ARGUMENT, "kv is NULL");
+  if (kv->head_dim != 128) return fail(HS_ERR_UNSUPPORTED, "head_dim %d (only 128 is supported)", kv->head_dim);
+  if (kv->dtype != HS_F32 && kv->dtype != HS_BF16 && kv->dtype != HS_FP8_E4M3)
+    return fail(HS_ERR_INVALID_ARGUMENT, "unknown cache dtype %d", (int)kv->dtype);
+  if (kv->num_kv_heads < 1) return fail(HS_ERR_INVALID_ARGUMENT, "num_kv_heads %d", kv->num_kv_heads);
+  if (!kv->k || !kv->v) return fail(HS_ERR_INVALID_ARGUMENT, "cache k/v pointer is NULL");
+  if (!aligned16(kv->k) || !aligned16(kv->v)) return fail(HS_ERR_INVALID_ARGUMENT, "cache k/v not 16-byte aligned");
+  const bool fp8 = kv->dtype == HS_FP8_E4M3;
+  if (fp8 != (kv->k_scale != nullptr) || fp8 != (kv->v_scale != nullptr))
+    return fail(HS_ERR_INVALID_ARGUMENT, "scale pointers must be given exactly for FP8 caches");
+  if (kv->capacity_rows < 1) return fail(HS_ERR_INVALID_ARGUMENT, "capacity_rows %lld", (long long)kv->capacity_rows);
+  ci.n_kv = kv->num_kv_heads;
+  ci.B = kv->batch;
+  ci.maxL = 0;
+  ci.total = 0;
+  if (!need_rows) return HS_OK;
+  if (kv->batch < 1) return fail(HS_ERR_INVALID_ARGUMENT, "batch %d", kv->batch);
+  if (!kv->d_row_start || !kv->h_row_start || !kv->d_seq_len || !kv->h_seq_len)
+    return fail(HS_ERR_INVALID_ARGUMENT, "row_start / seq_len pointer is NULL");
+  for (int b = 0; b < kv->batch; ++b) {
+    const int64_t L = kv->h_seq_len[b], r0 = kv->h_row_start[b];
+    if (L < 1) return fail(HS_ERR_INVALID_ARGUMENT, "seq_len[%d] = %lld < 1", b, (long long)L);
+    if (r0 < 0 || r0 + L > kv->capacity_rows)
+      return fail(HS_ERR_INVALID_ARGUMENT, "rows of sequence %d [%lld, %lld) outside capacity %lld", b,
+                  (long long)r0, (long long)(r0 + L), (long long)kv->capacity_rows);
+    ci.maxL = std::max<int>(ci.maxL, (int)L);
+    ci.total += L;
+  }
+  return HS_OK;
+}
+
+hs_status check_params(const hs_attn_params* p, int n_kv) {
+  if (!p) return fail(HS_ERR_INVALID_ARGUMENT, "params is NULL");
+  if (p->num_q_heads < 1 || p->num_q_heads % n_kv)
+    return fail(HS_ERR_INVALID_ARGUMENT, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
+                p->num_q_heads, n_kv);
+  if (p->q_tokens < 1) return fail(HS_ERR_INVALID_ARGUMENT, "q_tokens %d", p->q_tokens);
+  if (p->top_k < 0 || p->window < 0 || (int64_t)p->top_k + p->window < 1)
+    return fail(HS_ERR_INVALID_ARGUMENT, "top_k %d / window %d", p->top_k, p->window);
+  if (!(p->softmax_scale >= 0.f) || !isfinite(p->softmax_scale))
+    return fail(HS_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
+  return HS_OK;
+}
+
+float scale_log2(const hs_attn_params* p) {
+  const float s = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / sqrtf(128.0f);
+  return s * 1.4426950408889634f;
+}
+
+int kv_type(hs_dtype d) { return d == HS_F32 ? hs::KV_F32 : d == HS_BF16 ? hs::KV_BF16 : hs::KV_FP8; }
+
+// ---------------------------------------------------------------- plans
+
+struct FullPlan {
+  int ct, nwr, G, R, n_lists, chunk, max_chunks;
+  int nwr_s, chunk_s, max_chunks_s;
+  int64_t s_stride;
+  size_t off_acc, off_ml, off_lse2, off_scores, total;
+};
+
+int pow2_at_least(int x) { int p = 1; while (p < x) p <<= 1; return p; }
+
+hs_status plan_full(const hs_kv_cache* kv, const hs_attn_params* p, hs_dtype q_dtype, const CacheInfo& ci,
+                    FullPlan& pl) {
+  const int H = p->num_q_heads;
+  pl.G = H / ci.n_kv;
+  pl.R = p->q_tokens * pl.G;
+  pl.ct = (kv->dtype == HS_F32 || q_dtype == HS_F32) ? hs::CT_F32 : hs::CT_BF16;
+  if (!(pl.G % 32 == 0 || pl.G == 8 || pl.G == 16) || pl.G > 256)
+    return fail(HS_ERR_UNSUPPORTED, "heads per KV head G = %d: selection scores need G in {8, 16} or a "
+                "multiple of 32 up to 256", pl.G);
+  if (pl.ct == hs::CT_F32 && pl.G > 128)
+    return fail(HS_ERR_UNSUPPORTED, "fp32 queries/caches support at most 128 heads per KV head");
+  pl.nwr = pl.ct == hs::CT_F32 ? (pl.R <= 32 ? 1 : 4) : hs::rows_per_wave_group(pl.R);
+  pl.n_lists = ci.B * ci.n_kv;
+  const int tt = hs::partial_tile_tokens(pl.nwr);
+  const int zb = (pl.R + 32 * pl.nwr - 1) / (32 * pl.nwr);
+  int chunk = env_int("HS_SPLIT_TOKENS", 0);
+  if (chunk <= 0) {
+    // about 1024 work items over the whole batch, 512..16384 tokens each
+    const int64_t per = (ci.total * zb + 1023) / 1024;
+    chunk = (int)std::min<int64_t>(16384, std::max<int64_t>(512, per));
+  }
+  pl.chunk = (int)align_up((size_t)chunk, (size_t)tt);
+  pl.max_chunks = (ci.maxL + pl.chunk - 1) / pl.chunk;
+
+  int nwr_s = pl.ct == hs::CT_F32 ? (pl.R <= 32 ? 1 : pl.R <= 64 ? 2 : 4) : hs::rows_per_wave_group(pl.R);
+  nwr_s = std::max(nwr_s, pow2_at_least((pl.G + 31) / 32));
+  pl.nwr_s = nwr_s;
+  int maxc = 0;
+  for (int b = 0; b < ci.B; ++b) maxc = std::max(maxc, kv->h_seq_len[b] - std::min(p->window, kv->h_seq_len[b]));
+  pl.s_stride = maxc;
+  pl.chunk_s = pl.chunk;
+  pl.max_chunks_s = (maxc + pl.chunk_s - 1) / pl.chunk_s;
+
+  size_t off = 0;
+  pl.off_acc = off;
+  off += align_up((size_t)pl.n_lists * pl.max_chunks * pl.R * 128 * 4, 256);
+  pl.off_ml = off;
+  off += align_up((size_t)pl.n_lists * pl.max_chunks * pl.R * 2 * 4, 256);
+  pl.off_lse2 = off;
+  off += align_up((size_t)ci.B * p->q_tokens * H * 4, 256);
+  pl.off_scores = off;
+  off += align_up((size_t)ci.B * p->q_tokens * ci.n_kv * pl.s_stride * 4, 256);
+  pl.total = off;
+  return HS_OK;
+}
+
+struct SparsePlan {
+  int ct, nwr, G, n_lists, chunk, max_chunks, cap;
+  size_t off_acc, off_ml, total;
+};
+
+void plan_sparse(const hs_kv_cache* kv, const hs_attn_params* p, hs_dtype q_dtype, const CacheInfo& ci,
+                 SparsePlan& pl) {
+  pl.G = p->num_q_heads / ci.n_kv;
+  pl.ct = (kv->dtype == HS_F32 || q_dtype == HS_F32) ? hs::CT_F32 : hs::CT_BF16;
+  pl.nwr = pl.ct == hs::CT_F32 ? (pl.G <= 32 ? 1 : 4) : hs::rows_per_wave_group(pl.G);
+  pl.n_lists = ci.B * p->q_tokens * ci.n_kv;
+  pl.cap = p->top_k + p->window;
+  const int tt = hs::partial_tile_tokens(pl.nwr);
+  const int tiles = (pl.cap + tt - 1) / tt;
+  int per_list = std::max(1, std::min(tiles, (512 + pl.n_lists - 1) / pl.n_lists));
+  int chunk = env_int("HS_SPARSE_CHUNK", 0);
+  if (chunk <= 0) chunk = ((tiles + per_list - 1) / per_list) * tt;
+  pl.chunk = std::min((int)align_up((size_t)chunk, (size_t)tt), 1152);
+  pl.max_chunks = (pl.cap + pl.chunk - 1) / pl.chunk;
+  size_t off = 0;
+  pl.off_acc = off;
+  off += align_up((size_t)pl.n_lists * pl.max_chunks * pl.G * 128 * 4, 256);
+  pl.off_ml = off;
+  off += align_up((size_t)pl.n_lists * pl.max_chunks * pl.G * 2 * 4, 256);
+  pl.total = off;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hs_abi_version(void) { return HS_ABI_VERSION; }
+
+const char* hs_status_string(hs_status s) {
+  switch (s) {
+    case HS_OK: return "HS_OK";
+    case HS_ERR_INVALID_ARGUMENT: return "HS_ERR_INVALID_ARGUMENT";
+    case HS_ERR_UNSUPPORTED: return "HS_ERR_UNSUPPORTED";
+    case HS_ERR_WORKSPACE_TOO_SMALL: return "HS_ERR_WORKSPACE_TOO_SMALL";
+    case HS_ERR_HIP: return "HS_ERR_HIP";
+  }
+  return "unknown hs_status";
+}
+
+const char* hs_last_error(void) { return g_last_error.c_str(); }
+
+void hs_timing_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_timing = enable != 0;
+}
+
+int hs_timing_collect(hs_kernel_time* out, int max) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  int n = 0;
+  bool ok = true;
+  for (const TimeRec& r : g_recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) ok = false;
+    if (out && n < max) out[n++] = hs_kernel_time{r.name, ms};
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_recs.clear();
+  return ok ? n : -1;
+}
+
+size_t hs_full_attn_select_workspace_size(const hs_kv_cache* kv, const hs_attn_params* p) {
+  CacheInfo ci;
+  if (check_cache(kv, ci, true) != HS_OK || check_params(p, ci.n_kv) != HS_OK) return 0;
+  FullPlan pl;
+  // the plan depends on the query type only through the compute type; size for the larger
+  if (plan_full(kv, p, HS_F32, ci, pl) != HS_OK) return 0;
+  FullPlan pb;
+  if (plan_full(kv, p, HS_BF16, ci, pb) != HS_OK) return 0;
+  return std::max(pl.total, pb.total);
+}
+
+size_t hs_sparse_attn_workspace_size(const hs_kv_cache* kv, const hs_attn_params* p) {
+  CacheInfo ci;
+  if (check_cache(kv, ci, true) != HS_OK || check_params(p, ci.n_kv) != HS_OK) return 0;
+  SparsePlan a, b;
+  plan_sparse(kv, p, HS_F32, ci, a);
+  plan_sparse(kv, p, HS_BF16, ci, b);
+  return std::max(a.total, b.total);
+}
+
+size_t hs_select_workspace_size(int32_t, int32_t, int32_t, int32_t, int32_t, int32_t) { return 0; }
+
+hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, const void* q, hs_dtype q_dtype,
+                              float* out, float* lse, int32_t* sel_idx, int32_t* sel_count, float* scores_out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  CacheInfo ci;
+  hs_status st = check_cache(kv, ci, true);
+  if (st != HS_OK) return st;
+  if ((st = check_params(p, ci.n_kv)) != HS_OK) return st;
+  if (!q || !out || !sel_idx || !sel_count) return fail(HS_ERR_INVALID_ARGUMENT, "q/out/sel_idx/sel_count is NULL");
+  if (q_dtype != HS_F32 && q_dtype != HS_BF16) return fail(HS_ERR_INVALID_ARGUMENT, "q dtype must be F32 or BF16");
+  if (!aligned16(q)) return fail(HS_ERR_INVALID_ARGUMENT, "q not 16-byte aligned");
+  FullPlan pl;
+  if ((st = plan_full(kv, p, q_dtype, ci, pl)) != HS_OK) return st;
+  if (!workspace && pl.total) return fail(HS_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (workspace_bytes < pl.total)
+    return fail(HS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, pl.total);
+  if (!aligned16(workspace)) return fail(HS_ERR_INVALID_ARGUMENT, "workspace not 16-byte aligned");
+
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int kvt = kv_type(kv->dtype);
+  const float sl2 = scale_log2(p);
+  float* lse2 = (float*)(ws + pl.off_lse2);
+  float* scores = scores_out ? scores_out : (float*)(ws + pl.off_scores);
+
+  hs::AttnArgs a{};
+  a.k = kv->k; a.v = kv->v; a.k_scale = kv->k_scale; a.v_scale = kv->v_scale;
+  a.row_start = kv->d_row_start; a.seq_len = kv->d_seq_len;
+  a.q = q; a.q_f32 = q_dtype == HS_F32;
+  a.n_kv = ci.n_kv; a.H = p->num_q_heads; a.G = pl.G; a.n_q = p->q_tokens;
+  a.R = pl.R; a.n_lists = pl.n_lists; a.chunk = pl.chunk; a.max_chunks = pl.max_chunks;
+  a.scale_log2 = sl2;
+  a.part_acc = (float*)(ws + pl.off_acc); a.part_ml = (float*)(ws + pl.off_ml);
+  hipError_t e = timed("attn_partial_dense", s, [&] { return hs::launch_attn_partial(a, kvt, pl.ct, false, s); });
+  if (e != hipSuccess) return hip_fail(e, "full attention pass 1");
+
+  hs::MergeArgs m{};
+  m.part_acc = a.part_acc; m.part_ml = a.part_ml; m.seq_len = kv->d_seq_len; m.sel_count = nullptr;
+  m.gather = 0; m.n_kv = ci.n_kv; m.H = a.H; m.G = pl.G; m.n_q = a.n_q; m.R = pl.R; m.n_lists = pl.n_lists;
+  m.chunk = pl.chunk; m.max_chunks = pl.max_chunks; m.out = out; m.lse = lse; m.lse2 = lse2;
+  if ((e = timed("attn_merge_dense", s, [&] { return hs::launch_attn_merge(m, s); })) != hipSuccess)
+    return hip_fail(e, "full attention merge");
+
+  if (pl.max_chunks_s > 0) {
+    hs::ScoreArgs sa{};
+    sa.k = kv->k; sa.k_scale = kv->k_scale; sa.row_start = kv->d_row_start; sa.seq_len = kv->d_seq_len;
+    sa.q = q; sa.q_f32 = a.q_f32; sa.n_kv = ci.n_kv; sa.H = a.H; sa.G = pl.G; sa.n_q = a.n_q; sa.R = pl.R;
+    sa.n_lists = pl.n_lists; sa.window = p->window; sa.chunk = pl.chunk_s; sa.max_chunks = pl.max_chunks_s;
+    sa.scale_log2 = sl2; sa.lse2 = lse2; sa.scores = scores; sa.s_stride = pl.s_stride;
+    if ((e = timed("attn_scores", s, [&] { return hs::launch_attn_scores(sa, kvt, pl.ct, pl.nwr_s, s); })) != hipSuccess)
+      return hip_fail(e, "selection scores");
+  }
+
+  hs::SelectArgs se{};
+  se.scores = scores; se.s_stride = pl.s_stride; se.seq_len = kv->d_seq_len; se.n_q = p->q_tokens;
+  se.n_kv = ci.n_kv; se.top_k = p->top_k; se.window = p->window; se.cap = p->top_k + p->window;
+  se.sel_idx = sel_idx; se.sel_count = sel_count;
+  if ((e = timed("select_topk", s, [&] { return hs::launch_select(se, ci.B * p->q_tokens * ci.n_kv, s); })) != hipSuccess)
+    return hip_fail(e, "selection");
+  return HS_OK;
+}
+
+hs_status hs_sparse_attn(const hs_kv_cache* kv, const hs_attn_params* p, const void* q, hs_dtype q_dtype,
+                         const int32_t* sel_idx, const int32_t* sel_count, float* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  CacheInfo ci;
+  hs_status st = check_cache(kv, ci, true);
+  if (st != HS_OK) return st;
+  if ((st = check_params(p, ci.n_kv)) != HS_OK) return st;
+  if (!q || !out || !sel_idx || !sel_count) return fail(HS_ERR_INVALID_ARGUMENT, "q/out/sel_idx/sel_count is NULL");
+  if (q_dtype != HS_F32 && q_dtype != HS_BF16) return fail(HS_ERR_INVALID_ARGUMENT, "q dtype must be F32 or BF16");
+  if (!aligned16(q)) return fail(HS_ERR_INVALID_ARGUMENT, "q not 16-byte aligned");
+  if ((int64_t)p->top_k + p->window > 1152 * 64)
+    return fail(HS_ERR_UNSUPPORTED, "selection capacity %d too large", p->top_k + p->window);
+  SparsePlan pl;
+  plan_sparse(kv, p, q_dtype, ci, pl);
+  if (!workspace && pl.total) return fail(HS_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (workspace_bytes < pl.total)
+    return fail(HS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, pl.total);
+  if (!aligned16(workspace)) return fail(HS_ERR_INVALID_ARGUMENT, "workspace not 16-byte aligned");
+
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  hs::AttnArgs a{};
+  a.k = kv->k; a.v = kv->v; a.k_scale = kv->k_scale; a.v_scale = kv->v_scale;
+  a.row_start = kv->d_row_start; a.seq_len = kv->d_seq_len;
+  a.q = q; a.q_f32 = q_dtype == HS_F32;
+  a.n_kv = ci.n_kv; a.H = p->num_q_heads; a.G = pl.G; a.n_q = p->q_tokens;
+  a.R = pl.G; a.n_lists = pl.n_lists; a.chunk = pl.chunk; a.max_chunks = pl.max_chunks;
+  a.scale_log2 = scale_log2(p);
+  a.sel_idx = sel_idx; a.sel_count = sel_count; a.sel_cap = pl.cap;
+  a.part_acc = (float*)(ws + pl.off_acc); a.part_ml = (float*)(ws + pl.off_ml);
+  hipError_t e = timed("attn_partial_gather", s, [&] { return hs::launch_attn_partial(a, kv_type(kv->dtype), pl.ct, true, s); });
+  if (e != hipSuccess) return hip_fail(e, "sparse attention");
+  hs::MergeArgs m{};
+  m.part_acc = a.part_acc; m.part_ml = a.part_ml; m.seq_len = kv->d_seq_len; m.sel_count = sel_count;
+  m.sel_cap = pl.cap;
+  m.gather = 1; m.n_kv = ci.n_kv; m.H = a.H; m.G = pl.G; m.n_q = a.n_q; m.R = pl.G; m.n_lists = pl.n_lists;
+  m.chunk = pl.chunk; m.max_chunks = pl.max_chunks; m.out = out; m.lse = nullptr; m.lse2 = nullptr;
+  if ((e = timed("attn_merge_gather", s, [&] { return hs::launch_attn_merge(m, s); })) != hipSuccess)
+    return hip_fail(e, "sparse attention merge");
+  return HS_OK;
+}
+
+hs_status hs_select_from_scores(const float* scores, const int32_t* d_seq_len, const int32_t* h_seq_len,
+                                int32_t batch, int32_t q_tokens, int32_t n_kv, int32_t max_len, int32_t top_k,
+                                int32_t window, int32_t* sel_idx, int32_t* sel_count, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  (void)workspace; (void)workspace_bytes;
+  g_last_error.clear();
+  if (!scores || !d_seq_len || !h_seq_len || !sel_idx || !sel_count)
+    return fail(HS_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (batch < 1 || q_tokens < 1 || n_kv < 1 || max_len < 1)
+    return fail(HS_ERR_INVALID_ARGUMENT, "batch/q_tokens/n_kv/max_len must be >= 1");
+  if (top_k < 0 || window < 0 || (int64_t)top_k + window < 1)
+    return fail(HS_ERR_INVALID_ARGUMENT, "top_k %d / window %d", top_k, window);
+  for (int b = 0; b < batch; ++b)
+    if (h_seq_len[b] < 1 || h_seq_len[b] > max_len)
+      return fail(HS_ERR_INVALID_ARGUMENT, "seq_len[%d] = %d outside [1, max_len]", b, h_seq_len[b]);
+  hs::SelectArgs se{};
+  se.scores = scores; se.s_stride = max_len - std::min(window, max_len); se.seq_len = d_seq_len;
+  se.n_q = q_tokens; se.n_kv = n_kv; se.top_k = top_k; se.window = window; se.cap = top_k + window;
+  se.sel_idx = sel_idx; se.sel_count = sel_count;
+  hipError_t e = timed("select_topk", (hipStream_t)stream, [&] { return hs::launch_select(se, batch * q_tokens * n_kv, (hipStream_t)stream); });
+  if (e != hipSuccess) return hip_fail(e, "selection");
+  return HS_OK;
+}
+
+hs_status hs_kv_bridge(const void* hidden, int64_t n_tokens, int32_t d_model, int32_t n_targets,
+                       const void* const* w_k, const void* const* w_v, const hs_kv_cache* const* targets,
+                       int64_t row_offset, void* stream) {
+  g_last_error.clear();
+  if (!hidden || !w_k || !w_v || !targets) return fail(HS_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (n_tokens < 0) return fail(HS_ERR_INVALID_ARGUMENT, "n_tokens %lld", (long long)n_tokens);
+  if (d_model < 64 || d_model % 64) return fail(HS_ERR_INVALID_ARGUMENT, "d_model %d must be a positive multiple of 64", d_model);
+  if (n_targets < 1 || n_targets > 8) return fail(HS_ERR_UNSUPPORTED, "n_targets %d (1..8 supported)", n_targets);
+  if (row_offset < 0) return fail(HS_ERR_INVALID_ARGUMENT, "row_offset %lld", (long long)row_offset);
+  if (!aligned16(hidden)) return fail(HS_ERR_INVALID_ARGUMENT, "hidden not 16-byte aligned");
+  hs::BridgeArgs a{};
+  int fp8 = -1;
+  for (int l = 0; l < n_targets; ++l) {
+    const hs_kv_cache* t = targets[l];
+    if (!t || !w_k[l] || !w_v[l]) return fail(HS_ERR_INVALID_ARGUMENT, "target %d: NULL pointer", l);
+    CacheInfo ci;
+    hs_status st = check_cache(t, ci, false);
+    if (st != HS_OK) return st;
+    if (t->dtype != HS_BF16 && t->dtype != HS_FP8_E4M3)
+      return fail(HS_ERR_INVALID_ARGUMENT, "target %d: bridge output must be BF16 or FP8_E4M3", l);
+    if (t->num_kv_heads != 1) return fail(HS_ERR_UNSUPPORTED, "target %d: bridge targets have one KV head", l);
+    const int f = t->dtype == HS_FP8_E4M3;
+    if (fp8 >= 0 && f != fp8) return fail(HS_ERR_UNSUPPORTED, "all targets of one call must share a dtype");
+    fp8 = f;
+    if (row_offset + n_tokens > t->capacity_rows)
+      return fail(HS_ERR_INVALID_ARGUMENT, "target %d: rows [%lld, %lld) exceed capacity %lld", l,
+                  (long long)row_offset, (long long)(row_offset + n_tokens), (long long)t->capacity_rows);
+    if (!aligned16(w_k[l]) || !aligned16(w_v[l])) return fail(HS_ERR_INVALID_ARGUMENT, "target %d: weights not 16-byte aligned", l);
+    a.w[2 * l] = (const uint16_t*)w_k[l];
+    a.w[2 * l + 1] = (const uint16_t*)w_v[l];
+    a.out[2 * l] = t->k;
+    a.out[2 * l + 1] = t->v;
+    a.scale[2 * l] = t->k_scale;
+    a.scale[2 * l + 1] = t->v_scale;
+  }
+  if (n_tokens == 0) return HS_OK;
+  a.x = (const uint16_t*)hidden; a.T = n_tokens; a.Dm = d_model; a.n_targets = n_targets; a.fp8 = fp8;
+  a.row_offset = row_offset;
+  hipError_t e = timed("kv_bridge", (hipStream_t)stream, [&] { return hs::launch_bridge(a, (hipStream_t)stream); });
+  if (e != hipSuccess) return hip_fail(e, "kv bridge");
+  return HS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,163 @@
+// KV Bridging projection with fused cache-storage epilogue (gfx950 MFMA GEMM).
+//
+// ithome page "小米公开 MiMo-V3 核心架构 HySparse2", KV-sharing overview: each
+// Cross-Decoder full-attention layer builds its own K/V from the input hidden
+// state of the matching Self-Decoder full layer, with projections of its own;
+// prefill runs a single full-attention layer, so every target bridges from the
+// same source X (prefill early-exit paragraphs).  Per target l:
+//   K_l = X W_k[l],  V_l = X W_v[l]        X bf16 [T, Dm], W bf16 [Dm, 128]
+// stored at cache rows row_offset + t, as bf16 (round to nearest even) or as
+// OCP E4M3FN codes with one float32 scale per row (scale = amax / 448).
+//
+// Workgroup tile: 128 tokens x 256 columns (one target: K's 128 columns, then
+// V's), K-stage 64, 4 waves each owning 64 rows x 128 columns = one head block,
+// so a row's amax is reduced inside one wave.  MFMA v_mfma_f32_32x32x16_bf16,
+// operands from LDS (A rows of X; B as 16-bit transposed reads of W).
+
+#include "hs_common.hpp"
+#include "hs_internal.hpp"
+
+namespace hs {
+
+namespace {
+constexpr int BM = 128, BN = 256, BK = 64, NT = 256;
+constexpr int AROW = BK * 2 + 16;               // 144 B per X row in LDS
+constexpr int BROW = BN * 2 + 16;               // 528 B per k row of W in LDS
+constexpr int STAGE = BM * AROW + BK * BROW;    // 52224 B
+constexpr int EPI = 4 * 64 * 128 * 2;           // per-wave 64 x 128 bf16 staging
+constexpr int SMEM = STAGE > EPI ? STAGE : EPI;
+constexpr int APT = BM * BK * 2 / 16 / NT;      // X pieces per thread per stage (4)
+constexpr int BPT = BK * BN * 2 / 16 / NT;      // W pieces per thread per stage (8)
+
+__device__ __forceinline__ int crow(int lane, int r) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+}  // namespace
+
+__global__ __launch_bounds__(NT, 2) void bridge_kernel(BridgeArgs a) {
+  __shared__ __align__(16) char smem[SMEM];
+  char* const As = smem;
+  char* const Bs = smem + BM * AROW;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t m0 = (int64_t)blockIdx.x * BM;
+  const int tgt = blockIdx.y;
+  const uint16_t* wk = a.w[2 * tgt];
+  const uint16_t* wv = a.w[2 * tgt + 1];
+  const int Dm = a.Dm;
+
+  u32x4 ra[APT], rb[BPT];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < APT; ++i) {
+      const int p = tid + NT * i, row = p >> 3, c = p & 7;
+      const int64_t gr = m0 + row;
+      ra[i] = gr < a.T ? *(const u32x4*)(a.x + gr * Dm + k0 + c * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      const int p = tid + NT * i, kr = p >> 5, np = p & 31;
+      const uint16_t* src = (np < 16 ? wk : wv) + (int64_t)(k0 + kr) * D + (np & 15) * 8;
+      rb[i] = *(const u32x4*)src;
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < APT; ++i) {
+      const int p = tid + NT * i;
+      *(u32x4*)(As + (p >> 3) * AROW + (p & 7) * 16) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      const int p = tid + NT * i;
+      *(u32x4*)(Bs + (p >> 5) * BROW + (p & 31) * 16) = rb[i];
+    }
+  };
+
+  f32x16 acc[2][4] = {};
+  load(0);
+  for (int k0 = 0; k0 < Dm; k0 += BK) {
+    store();
+    __syncthreads();
+    if (k0 + BK < Dm) load(k0 + BK);
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      s16x8 av[2], bv[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        av[i] = *(const s16x8*)(As + (64 * wm + 32 * i + (lane & 31)) * AROW + (16 * s + 8 * (lane >> 5)) * 2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const char* bp = Bs + (16 * s + 8 * (lane >> 5)) * BROW + (128 * wn + 32 * j + (lane & 31)) * 2;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bv[j][e] = *(const short*)(bp + e * BROW);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[i]),
+                                                               __builtin_bit_cast(bf16x8, bv[j]), acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: this wave holds rows 64 wm + [0, 64) of head block (tgt, wn)
+  const int blk = 2 * tgt + wn;
+  char* const ep = smem + wave * (64 * 128 * 2);
+  const int64_t orow0 = a.row_offset + m0 + 64 * wm;
+  if (a.fp8) {
+    float* sc = a.scale[blk];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float am = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) am = fmaxf(am, fabsf(acc[i][j][r]));
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) am = fmaxf(am, __shfl_xor(am, o));
+        float scale = am / 448.0f;                                   // correctly rounded
+        if (scale == 0.f) scale = 1.f;
+        const int rl = 32 * i + crow(lane, r);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          ep[rl * 128 + 32 * j + (lane & 31)] = (char)f32_to_e4m3_rne(acc[i][j][r] / scale);
+        if ((lane & 31) == 0 && m0 + 64 * wm + rl < a.T) sc[orow0 + rl] = scale;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    char* dst = (char*)a.out[blk];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int p = lane + 64 * i, rl = p >> 3, c = p & 7;
+      if (m0 + 64 * wm + rl < a.T) *(u32x4*)(dst + (orow0 + rl) * 128 + c * 16) = *(const u32x4*)(ep + rl * 128 + c * 16);
+    }
+  } else {
+    uint16_t* e16 = (uint16_t*)ep;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          e16[(32 * i + crow(lane, r)) * 128 + 32 * j + (lane & 31)] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    char* dst = (char*)a.out[blk];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int p = lane + 64 * i, rl = p >> 4, c = p & 15;
+      if (m0 + 64 * wm + rl < a.T) *(u32x4*)(dst + (orow0 + rl) * 256 + c * 16) = *(const u32x4*)(ep + rl * 256 + c * 16);
+    }
+  }
+}
+
+hipError_t launch_bridge(const BridgeArgs& a, hipStream_t st) {
+  dim3 grid((unsigned)((a.T + BM - 1) / BM), a.n_targets);
+  hipLaunchKernelGGL(bridge_kernel, grid, dim3(NT), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace hs

@@ -1,0 +1,66 @@
+// Device-side helpers shared by the libhysparse kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hs {
+
+constexpr int D = 128;          // head dimension (the only one supported)
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// float32 -> bfloat16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// OCP E4M3FN code -> float32 (exact).  Normal codes move the 4-bit exponent
+// (bias 7) into binary32's (bias 127) and the 3 mantissa bits to the top of
+// its fraction; subnormal codes are m * 2^-9.  The two NaN codes are outside
+// the cache contract and decode as 480.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  uint32_t em = c & 0x7Fu;
+  float v = (em >= 8u) ? __uint_as_float((em + (120u << 3)) << 20) : (float)em * 0x1p-9f;
+  return __uint_as_float(__float_as_uint(v) | ((c & 0x80u) << 24));
+}
+
+// float32 -> OCP E4M3FN code: round to nearest, ties to the even mantissa,
+// saturating at +-448, zero magnitude -> 0x00.  With e = max(floor(log2|y|), -6)
+// the neighbours of |y| are multiples of 2^(e-3); q = rint(|y| * 2^(3-e)) is
+// exact (power-of-two scaling) and the magnitude code is ((e+7)<<3) + q - 8.
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne(float y) {
+  uint32_t u = __float_as_uint(y);
+  uint32_t a = u & 0x7FFFFFFFu;
+  if (a >= 0x43E00000u) return (u >> 24 & 0x80u) | 0x7Eu;     // |y| >= 448 (inf too)
+  int e = (int)(a >> 23) - 127;
+  e = e < -6 ? -6 : e;
+  float q = __builtin_rintf(__uint_as_float(a) * __uint_as_float((uint32_t)(127 + 3 - e) << 23));
+  int mag = ((e + 7) << 3) + (int)q - 8;
+  mag = mag > 0x7E ? 0x7E : mag;
+  if (mag == 0) return 0u;
+  return (u >> 24 & 0x80u) | (uint32_t)mag;
+}
+
+// Order-preserving uint32 key of a float32 (finite values; -0 sorts below +0).
+__device__ __forceinline__ uint32_t f32_key(float x) {
+  uint32_t b = __float_as_uint(x);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+}  // namespace hs

@@ -1,0 +1,92 @@
+// Internal argument blocks and launchers of libhysparse (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hs {
+
+enum KvType { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };       // cache storage type
+enum ComputeType { CT_BF16 = 0, CT_F32 = 1 };              // MFMA input type
+
+// attn_partial: one list = (b, g) in dense mode, (b, t, g) in gather mode.
+struct AttnArgs {
+  const void* k;
+  const void* v;
+  const float* k_scale;
+  const float* v_scale;
+  const int64_t* row_start;
+  const int32_t* seq_len;
+  const void* q;
+  int q_f32;
+  int n_kv, H, G, n_q;
+  int R;                 // query rows per list: n_q*G (dense) or G (gather)
+  int n_lists;
+  int chunk;             // tokens (dense) or list positions (gather) per work item
+  int max_chunks;
+  float scale_log2;      // softmax scale * log2(e)
+  const int32_t* sel_idx;
+  const int32_t* sel_count;
+  int sel_cap;
+  float* part_acc;       // [n_lists][max_chunks][R][128] unnormalised
+  float* part_ml;        // [n_lists][max_chunks][R][2]  (max in log2 units, sum)
+};
+
+struct MergeArgs {
+  const float* part_acc;
+  const float* part_ml;
+  const int32_t* seq_len;
+  const int32_t* sel_count;
+  int sel_cap;
+  int gather;
+  int n_kv, H, G, n_q, R, n_lists, chunk, max_chunks;
+  float* out;            // [B, n_q, H, 128]
+  float* lse;            // nullable, natural log
+  float* lse2;           // nullable, log2 units
+};
+
+struct ScoreArgs {
+  const void* k;
+  const float* k_scale;
+  const int64_t* row_start;
+  const int32_t* seq_len;
+  const void* q;
+  int q_f32;
+  int n_kv, H, G, n_q, R, n_lists, window, chunk, max_chunks;
+  float scale_log2;
+  const float* lse2;     // [B, n_q, H]
+  float* scores;         // [B, n_q, n_kv, s_stride]
+  int64_t s_stride;
+};
+
+struct SelectArgs {
+  const float* scores;   // [lists][s_stride]
+  int64_t s_stride;
+  const int32_t* seq_len;
+  int n_q, n_kv, top_k, window, cap;
+  int32_t* sel_idx;      // [lists][cap]
+  int32_t* sel_count;    // [lists]
+};
+
+struct BridgeArgs {
+  const uint16_t* x;     // [T, D] bf16
+  int64_t T;
+  int Dm;
+  int n_targets;
+  const uint16_t* w[16]; // per output head block of 128 columns: (target, K|V)
+  void* out[16];         // per block: cache k or v base pointer
+  float* scale[16];      // per block: FP8 scale base pointer or null
+  int fp8;
+  int64_t row_offset;
+};
+
+int rows_per_wave_group(int R);
+int partial_tile_tokens(int nwr);
+
+hipError_t launch_attn_partial(const AttnArgs& a, int kvt, int ct, bool gather, hipStream_t st);
+hipError_t launch_attn_merge(const MergeArgs& m, hipStream_t st);
+hipError_t launch_attn_scores(const ScoreArgs& a, int kvt, int ct, int nwr, hipStream_t st);
+hipError_t launch_select(const SelectArgs& a, int n_lists, hipStream_t st);
+hipError_t launch_bridge(const BridgeArgs& a, hipStream_t st);
+
+}  // namespace hs

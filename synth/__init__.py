@@ -143,10 +143,13 @@ def decode_case(cfg, L=None, B=None, seqs=None, block=0, lengths=None):
         if nn == 0:
             continue
         Lb = int(lens[i])
+        cnt = min(nn, Lb - WINDOW)                     # short sequences carry fewer needles
+        if cnt <= 0:
+            continue
         g = rng(cfg, T_NEEDLE + 100 * block, b)
-        pos = g.choice(Lb - WINDOW, size=nn, replace=False)
-        tok = g.integers(0, n_q, size=nn)
-        head = g.integers(0, H, size=nn)
+        pos = g.choice(Lb - WINDOW, size=cnt, replace=False)
+        tok = g.integers(0, n_q, size=cnt)
+        head = g.integers(0, H, size=cnt)
         for p, t, h in zip(pos, tok, head):
             kv_head = h // (H // n_kv)
             kf[row_start[i] + p, kv_head, :] = 4.0 * qf32[i, t, h, :]

@@ -1,0 +1,144 @@
+"""The C ABI library on the CPU: it loads, exports every entry point the header
+declares, and rejects invalid arguments synchronously, before any launch (only
+argument checks run here; nothing touches a GPU)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hysparse.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hs_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def hs():
+    from long_context_split_amd import hysparse
+    return hysparse
+
+
+def test_header_is_plain_c99():
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", HEADER],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run(["g++", "-std=c++17", "-Wall", "-Werror", "-fsyntax-only", "-x", "c++", HEADER],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_exports_every_declared_symbol(hs):
+    names = _declared_functions()
+    assert len(names) >= 10
+    out = subprocess.run(["nm", "-D", "--defined-only", hs.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (hs_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(hs.lib, n)
+
+
+def test_version_and_strings(hs):
+    assert hs.lib.hs_abi_version() == 1
+    assert hs.status_string(0) == "HS_OK"
+    assert hs.status_string(3) == "HS_ERR_WORKSPACE_TOO_SMALL"
+
+
+def _cache(hs, dtype=1, head_dim=128, n_kv=1, lens=(100, 200), cap=1000, scales=False, starts=None):
+    h_seq = np.asarray(lens, np.int32)
+    h_start = np.asarray(starts if starts is not None else np.concatenate([[0], np.cumsum(lens)[:-1]]), np.int64)
+    fake = 0x100000
+    c = hs.hs_kv_cache(dtype, head_dim, n_kv, len(lens), cap, fake, fake * 2,
+                       fake * 3 if scales else None, fake * 4 if scales else None, fake * 5,
+                       h_start.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), fake * 6,
+                       h_seq.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    c._keep = (h_seq, h_start)
+    return c
+
+
+def _call_full(hs, c, p, q=0x200000, ws=0x300000, nbytes=1 << 40, q_dtype=1):
+    return hs.lib.hs_full_attn_select(ctypes.byref(c), ctypes.byref(p), q, q_dtype, 0x400000, None, 0x500000,
+                                      0x600000, None, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (dict(head_dim=64), 2),
+    (dict(n_kv=0), 1),
+    (dict(lens=(0, 10)), 1),
+    (dict(lens=(600, 600)), 1),                 # rows past capacity
+    (dict(starts=(-1, 0)), 1),
+    (dict(dtype=2), 1),                         # FP8 without scale pointers
+    (dict(dtype=1, scales=True), 1),            # scales on a bf16 cache
+    (dict(dtype=7), 1),
+])
+def test_full_attn_select_rejects_bad_cache(hs, mutate, code):
+    c = _cache(hs, **mutate)
+    p = hs.params(32, 1)
+    assert _call_full(hs, c, p) == code
+    assert hs.last_error()
+
+
+def test_full_attn_select_rejects_bad_params(hs):
+    c = _cache(hs)
+    assert _call_full(hs, c, hs.params(31, 1)) == 2                # G = 31: unsupported group size
+    assert _call_full(hs, _cache(hs, n_kv=2), hs.params(33, 1)) == 1
+    assert _call_full(hs, c, hs.params(32, 0)) == 1
+    assert _call_full(hs, c, hs.params(32, 1, top_k=-1)) == 1
+    assert _call_full(hs, c, hs.params(32, 1, top_k=0, window=0)) == 1
+    assert _call_full(hs, c, hs.params(32, 1, softmax_scale=float("nan"))) == 1
+    assert _call_full(hs, c, hs.params(32, 1), q=0x200004) == 1   # misaligned q
+    assert _call_full(hs, c, hs.params(32, 1), q_dtype=2) == 1    # FP8 queries
+    assert _call_full(hs, c, hs.params(32, 1), q=None) == 1
+
+
+def test_workspace_size_and_too_small(hs):
+    c = _cache(hs)
+    p = hs.params(32, 1)
+    need = hs.lib.hs_full_attn_select_workspace_size(ctypes.byref(c), ctypes.byref(p))
+    assert need > 0
+    assert _call_full(hs, c, p, nbytes=need - 1) == 3
+    assert _call_full(hs, c, p, ws=None, nbytes=0) in (1, 3)
+    assert hs.lib.hs_sparse_attn_workspace_size(ctypes.byref(c), ctypes.byref(p)) > 0
+    bad = _cache(hs, head_dim=64)
+    assert hs.lib.hs_full_attn_select_workspace_size(ctypes.byref(bad), ctypes.byref(p)) == 0
+
+
+def test_sparse_attn_rejects(hs):
+    c = _cache(hs)
+    p = hs.params(32, 1)
+    f = hs.lib.hs_sparse_attn
+    assert f(ctypes.byref(c), ctypes.byref(p), 0x200000, 1, None, 0x500000, 0x400000, 0x300000, 1 << 40, None) == 1
+    assert f(ctypes.byref(c), ctypes.byref(p), 0x200000, 1, 0x700000, 0x500000, 0x400000, 0x300000, 0, None) == 3
+
+
+def test_select_from_scores_rejects(hs):
+    lens = np.array([10, 20], np.int32)
+    lp = lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    f = hs.lib.hs_select_from_scores
+    assert f(None, 0x100000, lp, 2, 1, 1, 20, 4, 2, 0x200000, 0x300000, None, 0, None) == 1
+    assert f(0x100000, 0x100000, lp, 2, 1, 1, 15, 4, 2, 0x200000, 0x300000, None, 0, None) == 1  # L > max_len
+    assert f(0x100000, 0x100000, lp, 2, 1, 1, 20, -1, 2, 0x200000, 0x300000, None, 0, None) == 1
+
+
+def test_bridge_rejects(hs):
+    t = _cache(hs, dtype=2, scales=True, lens=(1,), cap=1000)
+    t2 = _cache(hs, dtype=0, lens=(1,), cap=1000)
+    tp = (ctypes.POINTER(hs.hs_kv_cache) * 1)(ctypes.pointer(t))
+    tp2 = (ctypes.POINTER(hs.hs_kv_cache) * 1)(ctypes.pointer(t2))
+    w = (ctypes.c_void_p * 1)(0x800000)
+    f = hs.lib.hs_kv_bridge
+    assert f(0x900000, 100, 4096, 1, w, w, tp, 950, None) == 1        # offset + T > capacity
+    assert f(0x900000, 100, 4000, 1, w, w, tp, 0, None) == 1          # d_model not a multiple of 64
+    assert f(0x900000, 100, 4096, 1, w, w, tp2, 0, None) == 1         # fp32 target
+    assert f(0x900000, 100, 4096, 1, w, w, tp, -1, None) == 1
+    assert f(None, 100, 4096, 1, w, w, tp, 0, None) == 1
+    assert f(0x900000, 100, 4096, 9, w, w, tp, 0, None) == 2
+    assert f(0x900000, 0, 4096, 1, w, w, tp, 0, None) == 0            # nothing to do: no launch

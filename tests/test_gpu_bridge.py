@@ -1,0 +1,134 @@
+"""KV Bridging on the GPU against the oracle: identity weights make the bridge a
+pure quantiser (bit-exact codes and scales), random Xavier weights are held to
+the storage tolerances, and rows outside the written range are untouched."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import bridge as obridge, bf16 as obf16, e4m3 as oe4m3
+from gpu_cases import banner, dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+SENT8 = 0x5A
+SENTF = np.float32(-7.25)
+
+
+def _targets(n, cap, fp8):
+    from long_context_split_amd import hysparse as hs
+    tg = []
+    for _ in range(n):
+        if fp8:
+            k = torch.full((cap, 1, 128), SENT8, dtype=torch.uint8, device="cuda")
+            v = torch.full((cap, 1, 128), SENT8, dtype=torch.uint8, device="cuda")
+            ks = torch.full((cap, 1), float(SENTF), dtype=torch.float32, device="cuda")
+            vs = torch.full((cap, 1), float(SENTF), dtype=torch.float32, device="cuda")
+            tg.append(hs.KVCache(k, v, None, None, ks, vs))
+        else:
+            k = torch.full((cap, 1, 128), 0x1234, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+            v = torch.full((cap, 1, 128), 0x1234, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+            tg.append(hs.KVCache(k, v))
+    return tg
+
+
+def _host(t, fp8):
+    if fp8:
+        return (t.k.cpu().numpy()[:, 0], t.k_scale.cpu().numpy()[:, 0], t.v.cpu().numpy()[:, 0],
+                t.v_scale.cpu().numpy()[:, 0])
+    return t.k.view(torch.int16).cpu().numpy()[:, 0].view(np.uint16), None, \
+        t.v.view(torch.int16).cpu().numpy()[:, 0].view(np.uint16), None
+
+
+def _untouched(arr, r0, r1, sentinel):
+    return np.all(arr[:r0] == sentinel) and np.all(arr[r1:] == sentinel)
+
+
+@pytest.mark.parametrize("fp8", [True, False])
+def test_identity_weights_bit_exact(fp8):
+    banner(f"bridge identity W fp8={fp8}")
+    from long_context_split_amd import hysparse as hs
+    rng = np.random.default_rng(40)
+    T, off, cap = 1000, 37, 1200
+    x = synth.bf16_bits((rng.standard_normal((T, 128)) * np.exp(rng.uniform(-6, 6, (T, 1)))).astype(np.float32))
+    x[5] = 0                                               # an all-zero row: scale 1, codes 0
+    eye = synth.bf16_bits(np.eye(128, dtype=np.float32))
+    tg = _targets(2, cap, fp8)
+    hs.kv_bridge(dev_bf16(x), [dev_bf16(eye)] * 2, [dev_bf16(eye)] * 2, tg, off)
+    torch.cuda.synchronize()
+    ref = obridge.bridge(x, [eye], [eye], "e4m3" if fp8 else "bf16")[0]
+    for t in tg:
+        k, ks, v, vs = _host(t, fp8)
+        if fp8:
+            assert np.array_equal(k[off:off + T], ref["k"]) and np.array_equal(v[off:off + T], ref["v"])
+            assert np.array_equal(ks[off:off + T], ref["k_scale"]) and np.array_equal(vs[off:off + T], ref["v_scale"])
+            assert _untouched(k, off, off + T, SENT8) and _untouched(ks, off, off + T, SENTF)
+        else:
+            assert np.array_equal(k[off:off + T], x) and np.array_equal(v[off:off + T], x)
+            assert _untouched(k, off, off + T, 0x1234)
+
+
+def _check_random(case, tg, off, fp8, rows=None):
+    T = case["T"]
+    rows = np.arange(T) if rows is None else rows
+    xs = case["x"][rows]
+    ref = obridge.bridge(xs, case["w_k"], case["w_v"], "e4m3" if fp8 else "bf16")
+    eq_total = n_total = 0
+    for l, t in enumerate(tg):
+        k, ks, v, vs = _host(t, fp8)
+        for name, got, gsc in (("k", k, ks), ("v", v, vs)):
+            g = got[off + rows]
+            r = ref[l][name]
+            if fp8:
+                rs = ref[l][name + "_scale"]
+                gs = gsc[off + rows]
+                assert np.max(np.abs(gs / rs - 1)) <= 1e-5, "scale"
+                # ordinal distance between codes: sign-magnitude -> ordered integer
+                def ordn(c):
+                    c = c.astype(np.int32)
+                    return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+                dist = np.abs(ordn(g) - ordn(r))
+                assert dist.max() <= 1, "code more than one step from the oracle's"
+                eq_total += int(np.sum(dist == 0))
+                n_total += dist.size
+                assert _untouched(gsc, off, off + T, SENTF)
+            else:
+                d = np.abs(g.astype(np.int32) - r.astype(np.int32))
+                assert d.max() <= 1, "bf16 more than 1 ulp"
+                eq_total += int(np.sum(d == 0))
+                n_total += d.size
+    return eq_total / n_total
+
+
+@pytest.mark.parametrize("fp8", [True, False])
+def test_random_xavier_weights(fp8):
+    banner(f"bridge random W T=2000 D=512 targets=3 fp8={fp8}")
+    from long_context_split_amd import hysparse as hs
+    case = synth.bridge_case(4, T=2000, D=512, n_targets=3)
+    off, cap = 100, 2500
+    tg = _targets(3, cap, fp8)
+    hs.kv_bridge(dev_bf16(case["x"]), [dev_bf16(w) for w in case["w_k"]], [dev_bf16(w) for w in case["w_v"]],
+                 tg, off)
+    torch.cuda.synchronize()
+    frac = _check_random(case, tg, off, fp8)
+    assert frac >= 0.99
+    print(f"[result] bridge fp8={fp8} equal fraction {frac:.5f}", flush=True)
+
+
+@pytest.mark.slow
+def test_config4_full_size_sampled_rows():
+    """Config 4: 32768 tokens x 4096 -> 4 targets x (K, V), FP8, into 1M-row caches at
+    row 262144; the oracle checks 1024 sampled rows and the untouched rows."""
+    banner("bridge config 4 full size")
+    from long_context_split_amd import hysparse as hs
+    case = synth.bridge_case(4)
+    spec = case["spec"]
+    tg = _targets(4, spec["capacity"], True)
+    hs.kv_bridge(dev_bf16(case["x"]), [dev_bf16(w) for w in case["w_k"]], [dev_bf16(w) for w in case["w_v"]],
+                 tg, spec["offset"])
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(41).choice(case["T"], 1024, replace=False))
+    frac = _check_random(case, tg, spec["offset"], True, rows)
+    assert frac >= 0.99
+    print(f"[result] bridge config4 equal fraction {frac:.5f}", flush=True)

@@ -1,0 +1,85 @@
+"""Selection stage on the GPU, bit for bit against the oracle on identical float32
+score tensors (adversarial ties, plateaus, signs, zeros, subnormals, edge lengths)."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import selection
+from gpu_cases import banner
+
+pytestmark = pytest.mark.gpu
+
+
+def _pattern(kind, n, rng):
+    if kind == "random":
+        return rng.random(n).astype(np.float32)
+    if kind == "equal":
+        return np.full(n, 0.125, np.float32)
+    if kind == "plateau":       # a large block of ties straddles the k-th position
+        x = np.full(n, 0.5, np.float32)
+        x[rng.choice(n, min(n, 600), replace=False)] = 2.0
+        x[rng.choice(n, min(n, 3000), replace=False)] = 1.0
+        return x
+    if kind == "zeros":
+        return np.zeros(n, np.float32)
+    if kind == "signed":
+        x = rng.standard_normal(n).astype(np.float32)
+        x[::7] = -0.0
+        x[::11] = 0.0
+        return x
+    if kind == "subnormal":
+        return (rng.integers(0, 50, n) * np.float32(1e-45)).astype(np.float32)
+    if kind == "coarse":        # few distinct values -> many ties everywhere
+        return (rng.integers(0, 5, n) / 4).astype(np.float32)
+    raise ValueError(kind)
+
+
+KINDS = ["random", "equal", "plateau", "zeros", "signed", "subnormal", "coarse"]
+
+
+def _check(scores, lens, q_tokens, n_kv, top_k, window):
+    from long_context_split_amd import hysparse as hs
+    d = torch.from_numpy(scores).cuda()
+    idx, cnt = hs.select_from_scores(d, lens, q_tokens, n_kv, top_k, window)
+    torch.cuda.synchronize()
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    for b, L in enumerate(lens):
+        n = L - min(window, L)
+        for t in range(q_tokens):
+            for g in range(n_kv):
+                ri, rc = selection.select(scores[b, t, g, :n], L, top_k, window, f32_keys=True)
+                assert cnt[b, t, g] == rc, (b, t, g, L)
+                assert np.array_equal(idx[b, t, g], ri), (b, t, g, L)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_select_bit_exact_edge_lengths(kind):
+    banner(f"select kind={kind}")
+    lens = [1, 2, 127, 128, 129, 1151, 1152, 1153, 2000, 5000, 70001]
+    S = max(lens) - 128
+    rng = np.random.default_rng(100 + KINDS.index(kind))
+    scores = np.zeros((len(lens), 1, 1, S), np.float32)
+    for b, L in enumerate(lens):
+        n = L - min(128, L)
+        scores[b, 0, 0, :n] = _pattern(kind, n, rng)
+    _check(scores, lens, 1, 1, 1024, 128)
+
+
+def test_select_many_queries_and_kv_heads():
+    banner("select q_tokens=3 n_kv=2 small budgets")
+    rng = np.random.default_rng(7)
+    lens = [50, 300, 4099]
+    full = (rng.integers(0, 9, (3, 3, 2, max(lens))) / 8).astype(np.float32)
+    _check(np.ascontiguousarray(full[..., :max(lens) - 4]), lens, 3, 2, 16, 4)
+    _check(full, lens, 3, 2, 100, 0)
+
+
+def test_select_one_million_candidates():
+    banner("select L=1048576")
+    rng = np.random.default_rng(9)
+    L = 1 << 20
+    n = L - 128
+    x = (rng.random(n) * 1e-4).astype(np.float32)
+    x[rng.choice(n, 1500, replace=False)] = np.float32(3e-4)        # ties at the boundary
+    _check(x.reshape(1, 1, 1, n), [L], 1, 1, 1024, 128)
