@@ -44,6 +44,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle time budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="skip the Infinity Cache flush between steps")
+    ap.add_argument("--no-bridge", action="store_true", help="skip the KV Bridging measurement")
+    ap.add_argument("--bridge-iters", type=int, default=10)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB device-to-device copy (known bytes, for scaling HBM counters)")
     return ap.parse_args()
 
 
@@ -178,6 +182,16 @@ def main():
                 "algorithmic_bytes_per_launch": k1_bytes, "avg_launch_us": round(k1["avg_ms"] * 1e3, 2),
                 "dominant_kernel_by_time": dom}
 
+    # ---------------------------------------------------------------- KV Bridging (prefill side)
+    bridge = None if args.no_bridge else bench_bridge(dev, args.bridge_iters)
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration: 3 x 1 GiB device copies done")
+
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -211,10 +225,49 @@ def main():
                     for n, d in kern.items()},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "bridge": bridge,
         "timing": "HIP events per step; Infinity Cache flushed between steps" if flush is not None
         else "HIP events per step; no cache flush",
     }
     print(json.dumps(line), flush=True)
+
+
+def bench_bridge(dev, iters):
+    """KV Bridging of a 32768-token chunk: X [32768, 4096] bf16 x 4 targets x (W_k, W_v) [4096, 128],
+    stored as FP8 E4M3 + per-token scale into 1M-row caches at row 262144."""
+    import numpy as np
+    import torch
+    import synth
+    from long_context_split_amd import hysparse as hs
+    case = synth.bridge_case(4)
+    spec = case["spec"]
+    T, D, nt = case["T"], case["D"], case["n_targets"]
+    x = torch.from_numpy(case["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    wk = [torch.from_numpy(w.view(np.int16)).to(dev).view(torch.bfloat16) for w in case["w_k"]]
+    wv = [torch.from_numpy(w.view(np.int16)).to(dev).view(torch.bfloat16) for w in case["w_v"]]
+    cap = spec["capacity"]
+    tg = [hs.KVCache(torch.empty((cap, 1, 128), dtype=torch.uint8, device=dev),
+                     torch.empty((cap, 1, 128), dtype=torch.uint8, device=dev), None, None,
+                     torch.empty((cap, 1), dtype=torch.float32, device=dev),
+                     torch.empty((cap, 1), dtype=torch.float32, device=dev)) for _ in range(nt)]
+    for _ in range(2):
+        hs.kv_bridge(x, wk, wv, tg, spec["offset"])
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in evs:
+        a.record()
+        hs.kv_bridge(x, wk, wv, tg, spec["offset"])
+        b.record()
+    torch.cuda.synchronize()
+    ms = statistics.median(a.elapsed_time(b) for a, b in evs)
+    flops = 2.0 * T * D * nt * 2 * 128
+    tflops = flops / (ms * 1e-3) / 1e12
+    out_bytes = nt * 2 * T * (128 + 4)
+    in_bytes = T * D * 2 + nt * 2 * D * 128 * 2
+    log(f"bridge: {ms * 1e3:.1f} us  {tflops:.1f} TFLOP/s  ({tflops / 2500.0:.3f} of bf16 MFMA peak)")
+    return {"workload": "c4_bridge_32k: X[32768,4096] bf16 x 4 targets (K,V) -> FP8 E4M3 + per-token scale",
+            "ms": round(ms, 4), "tflops": round(tflops, 1), "bound": "mfma", "peak_tflops": 2500.0,
+            "frac": round(tflops / 2500.0, 4), "flops": flops, "bytes": in_bytes + out_bytes}
 
 
 def cpu_baseline(case, top_k, window, budget_s):

@@ -320,7 +320,7 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
   a.R = pl.R; a.n_lists = pl.n_lists; a.chunk = pl.chunk; a.max_chunks = pl.max_chunks;
   a.scale_log2 = sl2;
   a.part_acc = (float*)(ws + pl.off_acc); a.part_ml = (float*)(ws + pl.off_ml);
-  hipError_t e = timed("attn_partial_dense", s, [&] { return hs::launch_attn_partial(a, kvt, pl.ct, false, s); });
+  hipError_t e = timed("attn_partial_dense", s, [&] { return hs::launch_attn_partial(a, kvt, pl.ct, pl.nwr, false, s); });
   if (e != hipSuccess) return hip_fail(e, "full attention pass 1");
 
   hs::MergeArgs m{};
@@ -380,7 +380,7 @@ hs_status hs_sparse_attn(const hs_kv_cache* kv, const hs_attn_params* p, const v
   a.scale_log2 = scale_log2(p);
   a.sel_idx = sel_idx; a.sel_count = sel_count; a.sel_cap = pl.cap;
   a.part_acc = (float*)(ws + pl.off_acc); a.part_ml = (float*)(ws + pl.off_ml);
-  hipError_t e = timed("attn_partial_gather", s, [&] { return hs::launch_attn_partial(a, kv_type(kv->dtype), pl.ct, true, s); });
+  hipError_t e = timed("attn_partial_gather", s, [&] { return hs::launch_attn_partial(a, kv_type(kv->dtype), pl.ct, pl.nwr, true, s); });
   if (e != hipSuccess) return hip_fail(e, "sparse attention");
   hs::MergeArgs m{};
   m.part_acc = a.part_acc; m.part_ml = a.part_ml; m.seq_len = kv->d_seq_len; m.sel_count = sel_count;

@@ -621,8 +621,7 @@ int partial_tile_tokens(int nwr) { return nwr == 1 ? 128 : nwr == 2 ? 64 : 32; }
 int rows_per_wave_group(int R) { return R <= 32 ? 1 : R <= 64 ? 2 : R <= 128 ? 4 : 8; }
 
 template <bool GATHER>
-static hipError_t launch_partial_g(const AttnArgs& a, int kvt, int ct, hipStream_t st) {
-  const int nwr = rows_per_wave_group(a.R);
+static hipError_t launch_partial_g(const AttnArgs& a, int kvt, int ct, int nwr, hipStream_t st) {
   if (ct == CT_F32) {
     if (kvt == KV_F32) return launch_partial_shape<KV_F32, CT_F32, GATHER>(a, nwr, st);
     if (kvt == KV_BF16) return launch_partial_shape<KV_BF16, CT_F32, GATHER>(a, nwr, st);
@@ -633,8 +632,9 @@ static hipError_t launch_partial_g(const AttnArgs& a, int kvt, int ct, hipStream
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_attn_partial(const AttnArgs& a, int kvt, int ct, bool gather, hipStream_t st) {
-  return gather ? launch_partial_g<true>(a, kvt, ct, st) : launch_partial_g<false>(a, kvt, ct, st);
+hipError_t launch_attn_partial(const AttnArgs& a, int kvt, int ct, int nwr, bool gather, hipStream_t st) {
+  if (ct == CT_F32 && nwr != 1 && nwr != 4) return hipErrorInvalidValue;
+  return gather ? launch_partial_g<true>(a, kvt, ct, nwr, st) : launch_partial_g<false>(a, kvt, ct, nwr, st);
 }
 
 hipError_t launch_attn_merge(const MergeArgs& m, hipStream_t st) {

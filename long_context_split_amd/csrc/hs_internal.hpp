@@ -83,7 +83,8 @@ struct BridgeArgs {
 int rows_per_wave_group(int R);
 int partial_tile_tokens(int nwr);
 
-hipError_t launch_attn_partial(const AttnArgs& a, int kvt, int ct, bool gather, hipStream_t st);
+// nwr: query-row wave groups per workgroup, as planned by the host (1, 2, 4, 8; fp32 compute: 1 or 4)
+hipError_t launch_attn_partial(const AttnArgs& a, int kvt, int ct, int nwr, bool gather, hipStream_t st);
 hipError_t launch_attn_merge(const MergeArgs& m, hipStream_t st);
 hipError_t launch_attn_scores(const ScoreArgs& a, int kvt, int ct, int nwr, hipStream_t st);
 hipError_t launch_select(const SelectArgs& a, int n_lists, hipStream_t st);

@@ -55,7 +55,8 @@ def _check_seq(up, res, i, top_k=1024, window=128, check_sparse=True, stats=None
             if res["scores"] is not None:
                 gs = np.ascontiguousarray(res["scores"][i, t, g, :L - w])
                 # scores themselves: float32 of the float64 definition
-                assert np.abs(gs - ref["s"][t, g]).max() <= 1e-4 * max(1e-30, ref["s"][t, g].max()) + 1e-12
+                if L - w > 0:
+                    assert np.abs(gs - ref["s"][t, g]).max() <= 1e-4 * ref["s"][t, g].max() + 1e-12
                 gi, gc = selection.select(gs, L, top_k, window, f32_keys=True)          # G1
                 assert np.array_equal(res["idx"][i, t, g], gi), f"seq {i} t {t} g {g}: G1"
             h, n = recall(res["idx"][i, t, g], res["cnt"][i, t, g], ref["idx"][t, g], ref["cnt"][t, g], L,
