@@ -114,7 +114,7 @@ size_t hs_full_attn_select_workspace_size(const hs_kv_cache *kv, const hs_attn_p
 /* Workspace bytes hs_sparse_attn needs for these shapes (0 on invalid arguments). */
 size_t hs_sparse_attn_workspace_size(const hs_kv_cache *kv, const hs_attn_params *p);
 
-/* Workspace bytes hs_select_from_scores needs. */
+/* Workspace bytes hs_select_from_scores needs (0 on invalid arguments). */
 size_t hs_select_workspace_size(int32_t batch, int32_t q_tokens, int32_t n_kv, int32_t max_len,
                                 int32_t top_k, int32_t window);
 

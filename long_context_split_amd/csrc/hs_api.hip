@@ -145,10 +145,12 @@ int kv_type(hs_dtype d) { return d == HS_F32 ? hs::KV_F32 : d == HS_BF16 ? hs::K
 // ---------------------------------------------------------------- plans
 
 struct FullPlan {
+  int wave;  // 1: at most 32 query rows per KV head on a bf16 / FP8 cache -> attn_wave kernel
   int ct, nwr, G, R, n_lists, chunk, max_chunks;
   int nwr_s, chunk_s, max_chunks_s;
   int64_t s_stride;
-  size_t off_acc, off_ml, off_lse2, off_scores, total;
+  size_t off_acc, off_ml, off_lse2, off_scores, off_sel, total;
+  hs::SelectPlan sel;
 };
 
 int pow2_at_least(int x) { int p = 1; while (p < x) p <<= 1; return p; }
@@ -166,13 +168,20 @@ hs_status plan_full(const hs_kv_cache* kv, const hs_attn_params* p, hs_dtype q_d
     return fail(HS_ERR_UNSUPPORTED, "fp32 queries/caches support at most 128 heads per KV head");
   pl.nwr = pl.ct == hs::CT_F32 ? (pl.R <= 32 ? 1 : 4) : hs::rows_per_wave_group(pl.R);
   pl.n_lists = ci.B * ci.n_kv;
-  const int tt = hs::partial_tile_tokens(pl.nwr);
+  pl.wave = pl.ct == hs::CT_BF16 && pl.R <= 32;
+  const int tt = pl.wave ? 256 : hs::partial_tile_tokens(pl.nwr);
   const int zb = (pl.R + 32 * pl.nwr - 1) / (32 * pl.nwr);
   int chunk = env_int("HS_SPLIT_TOKENS", 0);
   if (chunk <= 0) {
-    // about 1024 work items over the whole batch, 512..16384 tokens each
-    const int64_t per = (ci.total * zb + 1023) / 1024;
-    chunk = (int)std::min<int64_t>(16384, std::max<int64_t>(512, per));
+    if (pl.wave) {
+      // about 512 workgroups (2 per CU-slot round), 1024..32768 tokens each
+      const int64_t per = (ci.total + 511) / 512;
+      chunk = (int)std::min<int64_t>(32768, std::max<int64_t>(1024, per));
+    } else {
+      // about 1024 work items over the whole batch, 512..16384 tokens each
+      const int64_t per = (ci.total * zb + 1023) / 1024;
+      chunk = (int)std::min<int64_t>(16384, std::max<int64_t>(512, per));
+    }
   }
   pl.chunk = (int)align_up((size_t)chunk, (size_t)tt);
   pl.max_chunks = (ci.maxL + pl.chunk - 1) / pl.chunk;
@@ -195,11 +204,15 @@ hs_status plan_full(const hs_kv_cache* kv, const hs_attn_params* p, hs_dtype q_d
   off += align_up((size_t)ci.B * p->q_tokens * H * 4, 256);
   pl.off_scores = off;
   off += align_up((size_t)ci.B * p->q_tokens * ci.n_kv * pl.s_stride * 4, 256);
+  hs::select_plan(pl.s_stride, pl.sel);
+  pl.off_sel = off;
+  off += align_up((size_t)ci.B * p->q_tokens * ci.n_kv * pl.sel.ws_stride * 4, 256);
   pl.total = off;
   return HS_OK;
 }
 
 struct SparsePlan {
+  int wave;  // 1: attn_wave (G <= 32, bf16/FP8 cache), partials merged by the last workgroup of a list
   int ct, nwr, G, n_lists, chunk, max_chunks, cap;
   size_t off_acc, off_ml, total;
 };
@@ -211,11 +224,13 @@ void plan_sparse(const hs_kv_cache* kv, const hs_attn_params* p, hs_dtype q_dtyp
   pl.nwr = pl.ct == hs::CT_F32 ? (pl.G <= 32 ? 1 : 4) : hs::rows_per_wave_group(pl.G);
   pl.n_lists = ci.B * p->q_tokens * ci.n_kv;
   pl.cap = p->top_k + p->window;
-  const int tt = hs::partial_tile_tokens(pl.nwr);
+  pl.wave = pl.ct == hs::CT_BF16 && pl.G <= 32;
+  const int tt = pl.wave ? 256 : hs::partial_tile_tokens(pl.nwr);   // attn_wave: 8 waves x 32 rows
   const int tiles = (pl.cap + tt - 1) / tt;
   int per_list = std::max(1, std::min(tiles, (512 + pl.n_lists - 1) / pl.n_lists));
   int chunk = env_int("HS_SPARSE_CHUNK", 0);
   if (chunk <= 0) chunk = ((tiles + per_list - 1) / per_list) * tt;
+  if (pl.wave && env_int("HS_SPARSE_CHUNK", 0) <= 0) chunk = pl.cap;   // one workgroup per list, no merge
   pl.chunk = std::min((int)align_up((size_t)chunk, (size_t)tt), 1152);
   pl.max_chunks = (pl.cap + pl.chunk - 1) / pl.chunk;
   size_t off = 0;
@@ -285,7 +300,13 @@ size_t hs_sparse_attn_workspace_size(const hs_kv_cache* kv, const hs_attn_params
   return std::max(a.total, b.total);
 }
 
-size_t hs_select_workspace_size(int32_t, int32_t, int32_t, int32_t, int32_t, int32_t) { return 0; }
+size_t hs_select_workspace_size(int32_t batch, int32_t q_tokens, int32_t n_kv, int32_t max_len, int32_t top_k,
+                                int32_t window) {
+  if (batch < 1 || q_tokens < 1 || n_kv < 1 || max_len < 1 || top_k < 0 || window < 0) return 0;
+  hs::SelectPlan sp;
+  hs::select_plan(max_len - std::min(window, max_len), sp);
+  return align_up((size_t)batch * q_tokens * n_kv * sp.ws_stride * 4, 256);
+}
 
 hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, const void* q, hs_dtype q_dtype,
                               float* out, float* lse, int32_t* sel_idx, int32_t* sel_count, float* scores_out,
@@ -320,15 +341,28 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
   a.R = pl.R; a.n_lists = pl.n_lists; a.chunk = pl.chunk; a.max_chunks = pl.max_chunks;
   a.scale_log2 = sl2;
   a.part_acc = (float*)(ws + pl.off_acc); a.part_ml = (float*)(ws + pl.off_ml);
-  hipError_t e = timed("attn_partial_dense", s, [&] { return hs::launch_attn_partial(a, kvt, pl.ct, pl.nwr, false, s); });
+  a.direct = pl.wave && pl.max_chunks == 1; a.out = out; a.lse = lse; a.lse2 = lse2;
+  const int n_sel_lists = ci.B * p->q_tokens * ci.n_kv;
+  if (pl.wave) {
+    a.zero_ptr = (uint32_t*)(ws + pl.off_sel);                 // the selection's histograms, cleared here
+    a.zero_stride = pl.sel.ws_stride;
+    a.zero_words = hs::SELECT_ZERO_WORDS;
+    a.zero_lists = n_sel_lists;
+  }
+  hipError_t e;
+  if (pl.wave)
+    e = timed("attn_wave_dense", s, [&] { return hs::launch_attn_wave(a, kvt, false, s); });
+  else
+    e = timed("attn_partial_dense", s, [&] { return hs::launch_attn_partial(a, kvt, pl.ct, pl.nwr, false, s); });
   if (e != hipSuccess) return hip_fail(e, "full attention pass 1");
 
   hs::MergeArgs m{};
   m.part_acc = a.part_acc; m.part_ml = a.part_ml; m.seq_len = kv->d_seq_len; m.sel_count = nullptr;
   m.gather = 0; m.n_kv = ci.n_kv; m.H = a.H; m.G = pl.G; m.n_q = a.n_q; m.R = pl.R; m.n_lists = pl.n_lists;
   m.chunk = pl.chunk; m.max_chunks = pl.max_chunks; m.out = out; m.lse = lse; m.lse2 = lse2;
-  if ((e = timed("attn_merge_dense", s, [&] { return hs::launch_attn_merge(m, s); })) != hipSuccess)
-    return hip_fail(e, "full attention merge");
+  if (!a.direct)                                                  // several chunks: merge them
+    if ((e = timed("attn_merge_dense", s, [&] { return hs::launch_attn_merge(m, s); })) != hipSuccess)
+      return hip_fail(e, "full attention merge");
 
   if (pl.max_chunks_s > 0) {
     hs::ScoreArgs sa{};
@@ -336,15 +370,24 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
     sa.q = q; sa.q_f32 = a.q_f32; sa.n_kv = ci.n_kv; sa.H = a.H; sa.G = pl.G; sa.n_q = a.n_q; sa.R = pl.R;
     sa.n_lists = pl.n_lists; sa.window = p->window; sa.chunk = pl.chunk_s; sa.max_chunks = pl.max_chunks_s;
     sa.scale_log2 = sl2; sa.lse2 = lse2; sa.scores = scores; sa.s_stride = pl.s_stride;
-    if ((e = timed("attn_scores", s, [&] { return hs::launch_attn_scores(sa, kvt, pl.ct, pl.nwr_s, s); })) != hipSuccess)
+    if (pl.wave) {
+      sa.hist = (uint32_t*)(ws + pl.off_sel);
+      sa.hist_stride = pl.sel.ws_stride;
+      if ((e = timed("scores_wave", s, [&] { return hs::launch_scores_wave(sa, kvt, s); })) != hipSuccess)
+        return hip_fail(e, "selection scores");
+    } else if ((e = timed("attn_scores", s, [&] { return hs::launch_attn_scores(sa, kvt, pl.ct, pl.nwr_s, s); })) !=
+               hipSuccess) {
       return hip_fail(e, "selection scores");
+    }
   }
 
   hs::SelectArgs se{};
   se.scores = scores; se.s_stride = pl.s_stride; se.seq_len = kv->d_seq_len; se.n_q = p->q_tokens;
   se.n_kv = ci.n_kv; se.top_k = p->top_k; se.window = p->window; se.cap = p->top_k + p->window;
   se.sel_idx = sel_idx; se.sel_count = sel_count;
-  if ((e = timed("select_topk", s, [&] { return hs::launch_select(se, ci.B * p->q_tokens * ci.n_kv, s); })) != hipSuccess)
+  se.ws = (uint32_t*)(ws + pl.off_sel); se.ws_stride = pl.sel.ws_stride; se.cand_off = pl.sel.cand_off;
+  se.chunk = pl.sel.chunk; se.max_chunks = pl.sel.max_chunks;
+  if ((e = timed("select_topk", s, [&] { return hs::launch_select(se, n_sel_lists, pl.wave, s); })) != hipSuccess)
     return hip_fail(e, "selection");
   return HS_OK;
 }
@@ -380,8 +423,17 @@ hs_status hs_sparse_attn(const hs_kv_cache* kv, const hs_attn_params* p, const v
   a.scale_log2 = scale_log2(p);
   a.sel_idx = sel_idx; a.sel_count = sel_count; a.sel_cap = pl.cap;
   a.part_acc = (float*)(ws + pl.off_acc); a.part_ml = (float*)(ws + pl.off_ml);
-  hipError_t e = timed("attn_partial_gather", s, [&] { return hs::launch_attn_partial(a, kv_type(kv->dtype), pl.ct, pl.nwr, true, s); });
-  if (e != hipSuccess) return hip_fail(e, "sparse attention");
+  if (pl.wave) {
+    a.direct = pl.max_chunks == 1; a.out = out; a.lse = nullptr; a.lse2 = nullptr;
+    hipError_t e = timed("attn_wave_gather", s, [&] { return hs::launch_attn_wave(a, kv_type(kv->dtype), true, s); });
+    if (e != hipSuccess) return hip_fail(e, "sparse attention");
+    if (a.direct) return HS_OK;
+  }
+  hipError_t e = hipSuccess;
+  if (!pl.wave) {
+    e = timed("attn_partial_gather", s, [&] { return hs::launch_attn_partial(a, kv_type(kv->dtype), pl.ct, pl.nwr, true, s); });
+    if (e != hipSuccess) return hip_fail(e, "sparse attention");
+  }
   hs::MergeArgs m{};
   m.part_acc = a.part_acc; m.part_ml = a.part_ml; m.seq_len = kv->d_seq_len; m.sel_count = sel_count;
   m.sel_cap = pl.cap;
@@ -396,7 +448,6 @@ hs_status hs_select_from_scores(const float* scores, const int32_t* d_seq_len, c
                                 int32_t batch, int32_t q_tokens, int32_t n_kv, int32_t max_len, int32_t top_k,
                                 int32_t window, int32_t* sel_idx, int32_t* sel_count, void* workspace,
                                 size_t workspace_bytes, void* stream) {
-  (void)workspace; (void)workspace_bytes;
   g_last_error.clear();
   if (!scores || !d_seq_len || !h_seq_len || !sel_idx || !sel_count)
     return fail(HS_ERR_INVALID_ARGUMENT, "NULL pointer argument");
@@ -407,11 +458,21 @@ hs_status hs_select_from_scores(const float* scores, const int32_t* d_seq_len, c
   for (int b = 0; b < batch; ++b)
     if (h_seq_len[b] < 1 || h_seq_len[b] > max_len)
       return fail(HS_ERR_INVALID_ARGUMENT, "seq_len[%d] = %d outside [1, max_len]", b, h_seq_len[b]);
+  const size_t need = hs_select_workspace_size(batch, q_tokens, n_kv, max_len, top_k, window);
+  if (!workspace) return fail(HS_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (workspace_bytes < need)
+    return fail(HS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(HS_ERR_INVALID_ARGUMENT, "workspace not 16-byte aligned");
   hs::SelectArgs se{};
   se.scores = scores; se.s_stride = max_len - std::min(window, max_len); se.seq_len = d_seq_len;
   se.n_q = q_tokens; se.n_kv = n_kv; se.top_k = top_k; se.window = window; se.cap = top_k + window;
   se.sel_idx = sel_idx; se.sel_count = sel_count;
-  hipError_t e = timed("select_topk", (hipStream_t)stream, [&] { return hs::launch_select(se, batch * q_tokens * n_kv, (hipStream_t)stream); });
+  hs::SelectPlan sp;
+  hs::select_plan(se.s_stride, sp);
+  se.ws = (uint32_t*)workspace; se.ws_stride = sp.ws_stride; se.cand_off = sp.cand_off;
+  se.chunk = sp.chunk; se.max_chunks = sp.max_chunks;
+  hipError_t e = timed("select_topk", (hipStream_t)stream,
+                       [&] { return hs::launch_select(se, batch * q_tokens * n_kv, false, (hipStream_t)stream); });
   if (e != hipSuccess) return hip_fail(e, "selection");
   return HS_OK;
 }

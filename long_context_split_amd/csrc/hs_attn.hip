@@ -26,143 +26,9 @@
 
 #include "hs_common.hpp"
 #include "hs_internal.hpp"
+#include "hs_mfma.hpp"
 
 namespace hs {
-
-// ---------------------------------------------------------------- MFMA policies
-
-// C/D layout of every 32x32 MFMA: lane l holds column (l & 31) and the 16 rows
-// 8*(r/4) + 4*(l>>5) + (r&3), r = 0..15.
-__device__ __forceinline__ int crow(int lane, int r) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
-
-template <int CT>
-struct Mma;
-
-// bf16 inputs, fp32 accumulate: v_mfma_f32_32x32x16_bf16.  Operand lane
-// layout: lane l supplies row/column (l & 31) and 8 consecutive k values;
-// the k index of element j is the same function of (l >> 5, j) for A and B,
-// so only consistency between the two operands matters.
-template <>
-struct Mma<CT_BF16> {
-  static constexpr int ROWB = 272;      // LDS bytes per token row: 256 + 16 pad (bank spread)
-  static constexpr int ESZ = 2;
-  struct QOp {
-    s16x8 v[8];                         // k-step s: d = 16 s + 8 (l >> 5) + j
-  };
-  __device__ static void load_q(QOp& q, const void* row, bool q_f32, bool valid, int lane) {
-    const int d0 = 8 * (lane >> 5);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      s16x8 t = {};
-      if (valid) {
-        if (q_f32) {
-          const float* p = (const float*)row + 16 * s + d0;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) t[j] = (short)f32_to_bf16_rne(p[j]);
-        } else {
-          t = *(const s16x8*)((const uint16_t*)row + 16 * s + d0);
-        }
-      }
-      q.v[s] = t;
-    }
-  }
-  // S^T = K Q^T for 32 tokens starting at ktile (LDS) and this wave's 32 rows.
-  __device__ static f32x16 qk_t(const char* ktile, const QOp& q, int lane) {
-    f32x16 acc = {};
-    const char* base = ktile + (lane & 31) * ROWB + (lane >> 5) * 16;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      s16x8 a = *(const s16x8*)(base + 32 * s);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                     __builtin_bit_cast(bf16x8, q.v[s]), acc, 0, 0, 0);
-    }
-    return acc;
-  }
-  // S = Q K^T (rows x tokens).
-  __device__ static f32x16 qk(const char* ktile, const QOp& q, int lane) {
-    f32x16 acc = {};
-    const char* base = ktile + (lane & 31) * ROWB + (lane >> 5) * 16;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      s16x8 b = *(const s16x8*)(base + 32 * s);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, q.v[s]),
-                                                     __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
-    }
-    return acc;
-  }
-  // O^T[d x rows] += V^T[d x tok] P^T[tok x rows]; p[r] is this lane's value
-  // for token crow(lane, r).  PV k-step u, element j <-> r = 8u + j.
-  template <bool SPLIT>
-  __device__ static void pv(f32x16 (&acc)[4], const char* vtile, const float (&p)[16], int lane) {
-    s16x8 ph[2], pl[2];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      uint32_t hb = f32_to_bf16_rne(p[r]);
-      ph[r >> 3][r & 7] = (short)hb;
-      if (SPLIT) pl[r >> 3][r & 7] = (short)f32_to_bf16_rne(p[r] - bf16_to_f32(hb));
-    }
-    const char* vb = vtile + (lane & 31) * 2 + (lane >> 5) * 4 * ROWB;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        s16x8 a;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          a[j] = *(const short*)(vb + 64 * mt + (16 * u + 8 * (j >> 2) + (j & 3)) * ROWB);
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                           __builtin_bit_cast(bf16x8, ph[u]), acc[mt], 0, 0, 0);
-        if (SPLIT)
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                             __builtin_bit_cast(bf16x8, pl[u]), acc[mt], 0, 0, 0);
-      }
-    }
-  }
-};
-
-// fp32 inputs: v_mfma_f32_32x32x2_f32.  Lane l supplies row/column (l & 31)
-// and the single k index (l >> 5) of each step.
-template <>
-struct Mma<CT_F32> {
-  static constexpr int ROWB = 516;      // 512 + 4: consecutive rows start one bank apart
-  static constexpr int ESZ = 4;
-  struct QOp {
-    float v[64];                        // step s: d = 2 s + (l >> 5)
-  };
-  __device__ static void load_q(QOp& q, const void* row, bool q_f32, bool valid, int lane) {
-    const int d0 = lane >> 5;
-#pragma unroll
-    for (int s = 0; s < 64; ++s) {
-      float x = 0.f;
-      if (valid) x = q_f32 ? ((const float*)row)[2 * s + d0] : bf16_to_f32(((const uint16_t*)row)[2 * s + d0]);
-      q.v[s] = x;
-    }
-  }
-  __device__ static f32x16 qk_t(const char* ktile, const QOp& q, int lane) {
-    f32x16 acc = {};
-    const float* base = (const float*)(ktile + (lane & 31) * ROWB) + (lane >> 5);
-#pragma unroll
-    for (int s = 0; s < 64; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(base[2 * s], q.v[s], acc, 0, 0, 0);
-    return acc;
-  }
-  __device__ static f32x16 qk(const char* ktile, const QOp& q, int lane) {
-    f32x16 acc = {};
-    const float* base = (const float*)(ktile + (lane & 31) * ROWB) + (lane >> 5);
-#pragma unroll
-    for (int s = 0; s < 64; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(q.v[s], base[2 * s], acc, 0, 0, 0);
-    return acc;
-  }
-  // step r pairs token crow(lane, r) of the two lane halves.
-  template <bool SPLIT>
-  __device__ static void pv(f32x16 (&acc)[4], const char* vtile, const float (&p)[16], int lane) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float* vr = (const float*)(vtile + crow(lane, r) * ROWB) + (lane & 31);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc[mt] = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[32 * mt], p[r], acc[mt], 0, 0, 0);
-    }
-  }
-};
 
 // ---------------------------------------------------------------- K/V super-tile loader
 
@@ -178,18 +44,14 @@ struct TileLoader {
   static constexpr int ROWB = Mma<CT>::ROWB;
   u32x4 reg[PPT];
 
-  // rowaddr(tok) -> byte pointer of that token's row, or nullptr when absent.
+  // rowaddr(tok) -> byte pointer of that token's row; always a valid row (absent tokens are
+  // clamped onto a present one and masked later), so the loads need no branch.
   template <class RowFn>
   __device__ void load(RowFn rowaddr, int tid) {
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
-      const int p = tid + i * NT;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (NP % NT == 0 || p < NP) {
-        const char* r = rowaddr(p / PPR);
-        if (r) x = *(const u32x4*)(r + (p % PPR) * 16);
-      }
-      reg[i] = x;
+      const int p = (NP % NT == 0) ? tid + i * NT : min(tid + i * NT, NP - 1);
+      reg[i] = *(const u32x4*)(rowaddr(p / PPR) + (p % PPR) * 16);
     }
   }
 
@@ -295,21 +157,21 @@ __global__ __launch_bounds__(64 * NWR * NWT) void attn_partial_kernel(AttnArgs a
   }
 
   TileLoader<KVT, CT, TT, NT> kl, vl;
-  auto tok_row = [&](int base, int tok) -> int {                  // cache row of tile token, -1 if none
-    const int pos = base + tok;
-    if (pos >= c1) return -1;
-    return GATHER ? gidx[pos - c0] : pos;
+  // cache row of a tile token, clamped into the chunk (absent tokens are masked in the softmax)
+  auto tok_row = [&](int base, int tok) -> int {
+    const int pos = min(base + tok, c1 - 1);
+    return GATHER ? max(gidx[pos - c0], 0) : pos;
   };
   auto issue = [&](int base) {
-    kl.load([&](int tok) -> const char* { int r = tok_row(base, tok); return r < 0 ? nullptr : kbase + (size_t)r * rstride; }, tid);
-    vl.load([&](int tok) -> const char* { int r = tok_row(base, tok); return r < 0 ? nullptr : vbase + (size_t)r * rstride; }, tid);
+    kl.load([&](int tok) -> const char* { return kbase + (size_t)tok_row(base, tok) * rstride; }, tid);
+    vl.load([&](int tok) -> const char* { return vbase + (size_t)tok_row(base, tok) * rstride; }, tid);
   };
   float sc_k = 0.f, sc_v = 0.f;
   auto issue_scales = [&](int base) {
-    if (FP8 && tid < TT) {
-      int r = tok_row(base, tid);
-      sc_k = r < 0 ? 0.f : a.k_scale[((size_t)rs + r) * a.n_kv + g];
-      sc_v = r < 0 ? 0.f : a.v_scale[((size_t)rs + r) * a.n_kv + g];
+    if (FP8) {
+      const size_t r = (size_t)rs + tok_row(base, tid % TT);
+      sc_k = a.k_scale[r * a.n_kv + g];
+      sc_v = a.v_scale[r * a.n_kv + g];
     }
   };
 
@@ -508,14 +370,10 @@ __global__ __launch_bounds__(64 * NWR * NWT) void attn_scores_kernel(ScoreArgs a
   // lse of this lane's 16 rows (rows 32 gr + crow(lane, r)); padding rows get +inf -> p = 0
   float lse2[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int rw = rb + 32 * gr + crow(lane, r);
-    if (rw < a.R) {
-      const int t = rw / a.G, hh = rw % a.G;
-      lse2[r] = a.lse2[((size_t)b * a.n_q + t) * a.H + (size_t)g * a.G + hh];
-    } else {
-      lse2[r] = INFINITY;
-    }
+  for (int r = 0; r < 16; ++r) {                                  // padding rows: +inf -> p = 0
+    const int rw = rb + 32 * gr + crow(lane, r), rc = min(rw, a.R - 1);
+    const float v = a.lse2[((size_t)b * a.n_q + rc / a.G) * a.H + (size_t)g * a.G + rc % a.G];
+    lse2[r] = rw < a.R ? v : INFINITY;
   }
   // local query tokens of the workgroup: rows [rb, rb + 32*NWR) hold tokens rb/G ..
   const int tpw = a.G >= 32 ? 1 : 32 / a.G;                        // query tokens per wave
@@ -524,12 +382,12 @@ __global__ __launch_bounds__(64 * NWR * NWT) void attn_scores_kernel(ScoreArgs a
   const int nt_wg = (min(a.R, rb + 32 * NWR) - rb + a.G - 1) / a.G;
 
   TileLoader<KVT, CT, TT, NT> kl;
-  auto issue = [&](int base) {
-    kl.load([&](int tok) -> const char* { const int pos = base + tok; return pos < c1 ? kbase + (size_t)pos * rstride : nullptr; }, tid);
+  auto issue = [&](int base) {                                    // clamped rows: no branch
+    kl.load([&](int tok) -> const char* { return kbase + (size_t)min(base + tok, c1 - 1) * rstride; }, tid);
   };
   float sc_k = 0.f;
   auto issue_scales = [&](int base) {
-    if (FP8 && tid < TT) { const int pos = base + tid; sc_k = pos < c1 ? a.k_scale[((size_t)rs + pos) * a.n_kv + g] : 0.f; }
+    if (FP8) sc_k = a.k_scale[((size_t)rs + min(base + tid % TT, c1 - 1)) * a.n_kv + g];
   };
   issue(c0);
   issue_scales(c0);

@@ -30,6 +30,13 @@ struct AttnArgs {
   int sel_cap;
   float* part_acc;       // [n_lists][max_chunks][R][128] unnormalised
   float* part_ml;        // [n_lists][max_chunks][R][2]  (max in log2 units, sum)
+  int direct;            // one chunk per list: write out / lse / lse2 instead of partials
+  float* out;            // [B, n_q, H, 128]
+  float* lse;            // nullable, natural log
+  float* lse2;           // nullable, log2 units
+  uint32_t* zero_ptr;    // attn_wave: words cleared by the grid (nullable):
+  int64_t zero_stride;   //   zero_lists runs of zero_words words, zero_stride apart
+  int zero_words, zero_lists;
 };
 
 struct MergeArgs {
@@ -57,6 +64,8 @@ struct ScoreArgs {
   const float* lse2;     // [B, n_q, H]
   float* scores;         // [B, n_q, n_kv, s_stride]
   int64_t s_stride;
+  uint32_t* hist;        // scores_wave: first-digit histograms of the selection (nullable),
+  int64_t hist_stride;   //   2048 words per list, hist_stride words apart
 };
 
 struct SelectArgs {
@@ -66,7 +75,16 @@ struct SelectArgs {
   int n_q, n_kv, top_k, window, cap;
   int32_t* sel_idx;      // [lists][cap]
   int32_t* sel_count;    // [lists]
+  uint32_t* ws;          // [lists][ws_stride] words (layout in hs_select.hip)
+  int64_t ws_stride, cand_off;
+  int chunk, max_chunks; // candidates per chunk workgroup, chunks per list
 };
+
+struct SelectPlan {
+  int chunk, max_chunks;
+  int64_t ws_stride, cand_off;   // words
+};
+void select_plan(int64_t s_stride, SelectPlan& p);
 
 struct BridgeArgs {
   const uint16_t* x;     // [T, D] bf16
@@ -85,9 +103,15 @@ int partial_tile_tokens(int nwr);
 
 // nwr: query-row wave groups per workgroup, as planned by the host (1, 2, 4, 8; fp32 compute: 1 or 4)
 hipError_t launch_attn_partial(const AttnArgs& a, int kvt, int ct, int nwr, bool gather, hipStream_t st);
+// attn_wave: R <= 32 query rows per list, bf16 or FP8 caches, 8 independent waves per workgroup
+hipError_t launch_attn_wave(const AttnArgs& a, int kvt, bool gather, hipStream_t st);
 hipError_t launch_attn_merge(const MergeArgs& m, hipStream_t st);
 hipError_t launch_attn_scores(const ScoreArgs& a, int kvt, int ct, int nwr, hipStream_t st);
-hipError_t launch_select(const SelectArgs& a, int n_lists, hipStream_t st);
+// fused_prefix: the histogram words were cleared and the first-digit histogram built by the
+// kernels before (attn_wave's zero hook, scores_wave); otherwise the select does both itself.
+hipError_t launch_select(const SelectArgs& a, int n_lists, bool fused_prefix, hipStream_t st);
+hipError_t launch_scores_wave(const ScoreArgs& a, int kvt, hipStream_t st);
+constexpr int SELECT_ZERO_WORDS = 4100;   // per-list words the selection needs cleared
 hipError_t launch_bridge(const BridgeArgs& a, hipStream_t st);
 
 }  // namespace hs

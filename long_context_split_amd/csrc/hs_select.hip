@@ -7,166 +7,321 @@
 // order of the scores with ties going to the lower index; the emitted list is
 // the global set in ascending index order, then the window rows, then -1.
 //
-// One 1024-thread workgroup per list (b, t, g):
-//   1. radix select on the order-preserving uint32 key of each float score,
-//      three LDS histogram passes (11 + 11 + 10 bits), each restricted to the
-//      key prefix fixed so far -> T = exact k'-th largest key and `need` =
-//      how many keys equal to T belong to the set;
-//   2. compaction in index order: every element with key > T, plus the first
-//      `need` elements with key == T; block-wide exclusive scans give each
-//      thread its output offset, so the list comes out ascending with no sort.
+// Multi-workgroup radix select on the order-preserving uint32 key of each
+// score, so that every list is spread over many CUs:
+//   sel_zero      clears the per-list histograms and counters (workspace)
+//   sel_hist1     per chunk: LDS histogram of the top 11 key bits -> global
+//   sel_cand      per chunk: finds the boundary bin b1 of the k'-th key, counts
+//                 keys above it per chunk, appends the keys inside it to a
+//                 candidate buffer and histograms their next 11 bits
+//   sel_finalize  per list: resolves the remaining 21 bits on the candidates ->
+//                 exact k'-th key T and the number `need` of keys == T taken
+//                 (lowest indices first); per-chunk output offsets; window part
+//   sel_write     per chunk: index-ordered compaction with block scans, so the
+//                 list comes out ascending with no sort
+// Counts are integers, so the result does not depend on atomic ordering.
+
+#include <algorithm>
 
 #include "hs_common.hpp"
 #include "hs_internal.hpp"
 
 namespace hs {
 
-constexpr int SEL_NT = 1024;
-constexpr int SEL_NW = SEL_NT / 64;
+namespace {
 
-// Block-wide exclusive scan of one uint per thread; also returns the total.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t& total) {
+constexpr int CH_NT = 256;                 // threads of the per-chunk kernels
+constexpr int FIN_NT = 1024;               // threads of the per-list kernel
+
+struct ListInfo {
+  int n;       // candidates L - W'
+  int kk;      // global budget k'
+  int w;       // window rows W'
+};
+
+__device__ __forceinline__ ListInfo list_info(const SelectArgs& a, int list) {
+  const int b = list / (a.n_q * a.n_kv);
+  const int Lb = a.seq_len[b];
+  ListInfo li;
+  li.w = min(a.window, Lb);
+  li.n = Lb - li.w;
+  li.kk = max(0, min(a.top_k, Lb - a.window));
+  return li;
+}
+
+// per-list workspace words: two 2048-bin histograms, candidate count, T, need,
+// then 4 arrays of max_chunks words (keys above the boundary bin, output offset,
+// ties before, selected count), then the (key, index) candidate pairs
+__device__ __forceinline__ uint32_t* ws_list(const SelectArgs& a, int list) { return a.ws + (size_t)list * a.ws_stride; }
+constexpr int W_HIST1 = 0, W_HIST2 = 2048, W_CCOUNT = 4096, W_T = 4097, W_NEED = 4098, W_ZERO = 4100, W_CHUNKS = 4100;
+
+template <int NT>
+__device__ __forceinline__ uint32_t block_scan_excl(uint32_t v, uint32_t* sh, uint32_t& total, bool reverse) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t incl = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
+    const uint32_t y = reverse ? __shfl_down(incl, o) : __shfl_up(incl, o);
+    if (reverse ? (lane + o < 64) : (lane >= o)) incl += y;
   }
-  if (lane == 63) wsum[wave] = incl;
+  if (lane == (reverse ? 0 : 63)) sh[wave] = incl;
   __syncthreads();
   if (wave == 0) {
-    uint32_t x = lane < SEL_NW ? wsum[lane] : 0u;
+    const uint32_t x = lane < NW ? sh[lane] : 0u;
     uint32_t xi = x;
 #pragma unroll
-    for (int o = 1; o < SEL_NW; o <<= 1) {
-      uint32_t y = __shfl_up(xi, o);
-      if (lane >= o) xi += y;
+    for (int o = 1; o < NW; o <<= 1) {
+      const uint32_t y = reverse ? __shfl_down(xi, o) : __shfl_up(xi, o);
+      if (reverse ? (lane + o < NW) : (lane >= o)) xi += y;
     }
-    if (lane < SEL_NW) wsum[SEL_NW + lane] = xi - x;       // exclusive prefix of wave totals
-    if (lane == SEL_NW - 1) wsum[2 * SEL_NW] = xi;
+    if (lane < NW) sh[NW + lane] = xi - x;
+    if (lane == (reverse ? 0 : NW - 1)) sh[2 * NW] = xi;
   }
   __syncthreads();
-  const uint32_t r = wsum[SEL_NW + wave] + incl - v;
-  total = wsum[2 * SEL_NW];
+  const uint32_t r = sh[NW + wave] + incl - v;
+  total = sh[2 * NW];
   __syncthreads();
   return r;
 }
 
-// Same, in reverse thread order: returns the sum over threads with a larger index.
-__device__ __forceinline__ uint32_t block_excl_scan_rev(uint32_t v, uint32_t* wsum, uint32_t& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t incl = v;                                           // sum over lanes >= lane
+// Digit d of a NB-bin histogram with (#keys in bins above d) < rem <= (# in bins >= d);
+// rem_out = rem minus the keys above d.  Every thread of the block gets the result.
+template <int NT, int NB>
+__device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t rem, uint32_t* sh, uint32_t& digit,
+                                           uint32_t& rem_out) {
+  constexpr int PER = NB / NT;
+  const int t = threadIdx.x;
+  uint32_t h[PER], sum = 0;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_down(incl, o);
-    if (lane + o < 64) incl += y;
+  for (int i = 0; i < PER; ++i) {
+    h[i] = hist[t * PER + i];
+    sum += h[i];
   }
-  if (lane == 0) wsum[wave] = incl;
-  __syncthreads();
-  if (wave == 0) {
-    uint32_t x = lane < SEL_NW ? wsum[lane] : 0u;
-    uint32_t xi = x;
+  uint32_t tot;
+  uint32_t above = block_scan_excl<NT>(sum, sh, tot, true);      // keys in bins of higher threads
 #pragma unroll
-    for (int o = 1; o < SEL_NW; o <<= 1) {
-      uint32_t y = __shfl_down(xi, o);
-      if (lane + o < SEL_NW) xi += y;
+  for (int i = PER - 1; i >= 0; --i) {
+    if (above < rem && rem <= above + h[i]) {
+      sh[3 * (NT / 64) + 1] = (uint32_t)(t * PER + i);
+      sh[3 * (NT / 64) + 2] = rem - above;
     }
-    if (lane < SEL_NW) wsum[SEL_NW + lane] = xi - x;           // sum over waves above
-    if (lane == 0) wsum[2 * SEL_NW] = xi;
+    above += h[i];
   }
   __syncthreads();
-  const uint32_t r = wsum[SEL_NW + wave] + incl - v;
-  total = wsum[2 * SEL_NW];
+  digit = sh[3 * (NT / 64) + 1];
+  rem_out = sh[3 * (NT / 64) + 2];
   __syncthreads();
-  return r;
 }
 
-__global__ __launch_bounds__(SEL_NT) void select_kernel(SelectArgs a) {
+}  // namespace
+
+__global__ __launch_bounds__(CH_NT) void sel_zero_kernel(SelectArgs a) {
+  uint32_t* w = ws_list(a, blockIdx.x);
+  for (int i = threadIdx.x; i < W_ZERO; i += CH_NT) w[i] = 0u;
+}
+
+__global__ __launch_bounds__(CH_NT) void sel_hist1_kernel(SelectArgs a) {
+  const int list = blockIdx.y;
+  const ListInfo li = list_info(a, list);
+  if (li.kk == 0 || li.kk >= li.n) return;
+  const int c0 = blockIdx.x * a.chunk;
+  if (c0 >= li.n) return;
+  const int c1 = min(li.n, c0 + a.chunk);
   __shared__ uint32_t hist[2048];
-  __shared__ uint32_t wsum[2 * SEL_NW + 1];
-  __shared__ uint32_t found[2];
-  const int tid = threadIdx.x;
-  const int list = blockIdx.x;
-  const int b = list / (a.n_q * a.n_kv);
-  const int Lb = a.seq_len[b];
-  const int w = min(a.window, Lb);
-  const int n = Lb - w;
-  const int kk = max(0, min(a.top_k, Lb - a.window));
+  for (int i = threadIdx.x; i < 2048; i += CH_NT) hist[i] = 0u;
+  __syncthreads();
   const float* s = a.scores + (size_t)list * a.s_stride;
-  int32_t* out = a.sel_idx + (size_t)list * a.cap;
-
-  if (kk >= n) {
-    for (int i = tid; i < n; i += SEL_NT) out[i] = i;         // every candidate selected
-  } else if (kk > 0) {
-    uint32_t prefix = 0u, pmask = 0u, rem = (uint32_t)kk;
-    const int shifts[3] = {21, 10, 0};
-    const uint32_t dmasks[3] = {0x7FFu, 0x7FFu, 0x3FFu};
-    for (int pass = 0; pass < 3; ++pass) {
-      const int sh = shifts[pass];
-      const uint32_t dm = dmasks[pass];
-      hist[2 * tid] = 0u;
-      hist[2 * tid + 1] = 0u;
-      __syncthreads();
-      for (int j = tid; j < n; j += SEL_NT) {
-        const uint32_t key = f32_key(s[j]);
-        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & dm], 1u);
-      }
-      __syncthreads();
-      // thread t owns bins 2t, 2t+1; count of keys in bins above them = reverse exclusive scan
-      const uint32_t h1 = hist[2 * tid + 1], h0 = hist[2 * tid];
-      uint32_t tot;
-      const uint32_t above = block_excl_scan_rev(h0 + h1, wsum, tot);
-      if (above < rem && rem <= above + h1) {
-        found[0] = 2u * tid + 1u;
-        found[1] = rem - above;
-      } else if (above + h1 < rem && rem <= above + h1 + h0) {
-        found[0] = 2u * tid;
-        found[1] = rem - above - h1;
-      }
-      __syncthreads();
-      prefix |= found[0] << sh;
-      pmask |= dm << sh;
-      rem = found[1];
-      __syncthreads();
-    }
-    const uint32_t T = prefix;
-    const uint32_t need = rem;                                 // keys == T to take, lowest index first
-    uint32_t written = 0u, ties_before = 0u;
-    constexpr int E = 4;
-    for (int start = 0; start < n && written < (uint32_t)kk; start += SEL_NT * E) {
-      const int j0 = start + tid * E;
-      uint32_t gt = 0u, eq = 0u;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        if (j0 + e < n) {
-          const uint32_t key = f32_key(s[j0 + e]);
-          gt |= (key > T ? 1u : 0u) << e;
-          eq |= (key == T ? 1u : 0u) << e;
-        }
-      }
-      uint32_t tot_eq, tot_sel;
-      const uint32_t eq_rank = ties_before + block_excl_scan(__builtin_popcount(eq), wsum, tot_eq);
-      uint32_t sel = gt, r = eq_rank;
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        if ((eq >> e) & 1u) { if (r < need) sel |= 1u << e; ++r; }
-      uint32_t pos = written + block_excl_scan(__builtin_popcount(sel), wsum, tot_sel);
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        if ((sel >> e) & 1u) { if (pos < (uint32_t)kk) out[pos] = j0 + e; ++pos; }
-      written += tot_sel;
-      ties_before += tot_eq;
-    }
-  }
-  for (int i = tid; i < w; i += SEL_NT) out[kk + i] = n + i;  // recent window rows L-W' .. L-1
-  for (int i = kk + w + tid; i < a.cap; i += SEL_NT) out[i] = -1;
-  if (tid == 0) a.sel_count[list] = kk + w;
+  for (int j = c0 + threadIdx.x; j < c1; j += CH_NT) atomicAdd(&hist[f32_key(s[j]) >> 21], 1u);
+  __syncthreads();
+  uint32_t* g = ws_list(a, list) + W_HIST1;
+  for (int i = threadIdx.x; i < 2048; i += CH_NT)
+    if (hist[i]) atomicAdd(&g[i], hist[i]);
 }
 
-hipError_t launch_select(const SelectArgs& a, int n_lists, hipStream_t st) {
-  hipLaunchKernelGGL(select_kernel, dim3(n_lists), dim3(SEL_NT), 0, st, a);
+__global__ __launch_bounds__(CH_NT) void sel_cand_kernel(SelectArgs a) {
+  const int list = blockIdx.y;
+  const ListInfo li = list_info(a, list);
+  if (li.kk == 0 || li.kk >= li.n) return;
+  const int c0 = blockIdx.x * a.chunk;
+  if (c0 >= li.n) return;
+  const int c1 = min(li.n, c0 + a.chunk);
+  __shared__ uint32_t sh[3 * (CH_NT / 64) + 3];
+  __shared__ uint32_t hist2[2048];
+  uint32_t* w = ws_list(a, list);
+  uint32_t b1, rem1;
+  find_digit<CH_NT, 2048>(w + W_HIST1, (uint32_t)li.kk, sh, b1, rem1);
+  for (int i = threadIdx.x; i < 2048; i += CH_NT) hist2[i] = 0u;
+  __syncthreads();
+  const float* s = a.scores + (size_t)list * a.s_stride;
+  uint2* cand = (uint2*)(w + a.cand_off);
+  const int lane = threadIdx.x & 63;
+  uint32_t gt = 0;
+  for (int j0 = c0; j0 < c1; j0 += CH_NT) {                      // uniform trip count for the ballot
+    const int j = j0 + threadIdx.x;
+    uint32_t key = 0u;
+    bool in = false;
+    if (j < c1) {
+      key = f32_key(s[j]);
+      const uint32_t d1 = key >> 21;
+      gt += d1 > b1 ? 1u : 0u;
+      in = d1 == b1;
+    }
+    const uint64_t m = __ballot(in);
+    if (m) {
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&w[W_CCOUNT], (uint32_t)__popcll(m));
+      base = __shfl(base, 0);
+      if (in) {
+        const uint32_t slot = base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+        cand[slot] = make_uint2(key, (uint32_t)j);
+        atomicAdd(&hist2[(key >> 10) & 0x7FFu], 1u);
+      }
+    }
+  }
+  uint32_t tot;
+  block_scan_excl<CH_NT>(gt, sh, tot, false);
+  if (threadIdx.x == 0) w[W_CHUNKS + blockIdx.x] = tot;           // keys above the boundary bin
+  __syncthreads();
+  for (int i = threadIdx.x; i < 2048; i += CH_NT)
+    if (hist2[i]) atomicAdd(&w[W_HIST2 + i], hist2[i]);
+}
+
+__global__ __launch_bounds__(FIN_NT) void sel_finalize_kernel(SelectArgs a) {
+  const int list = blockIdx.x;
+  const ListInfo li = list_info(a, list);
+  int32_t* out = a.sel_idx + (size_t)list * a.cap;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < li.w; i += FIN_NT) out[li.kk + i] = li.n + i;   // window rows L-W' .. L-1
+  for (int i = li.kk + li.w + tid; i < a.cap; i += FIN_NT) out[i] = -1;
+  if (tid == 0) a.sel_count[list] = li.kk + li.w;
+  if (li.kk == 0 || li.kk >= li.n) return;
+
+  __shared__ uint32_t sh[3 * (FIN_NT / 64) + 3];
+  __shared__ uint32_t hist3[1024];
+  __shared__ uint32_t gtx[1024], eqc[1024];
+  uint32_t* w = ws_list(a, list);
+  uint32_t b1, rem1, b2, rem2, b3, rem3;
+  find_digit<FIN_NT, 2048>(w + W_HIST1, (uint32_t)li.kk, sh, b1, rem1);
+  find_digit<FIN_NT, 2048>(w + W_HIST2, rem1, sh, b2, rem2);
+  hist3[tid] = 0u;
+  gtx[tid] = 0u;
+  eqc[tid] = 0u;
+  __syncthreads();
+  const uint32_t nc = w[W_CCOUNT];
+  const uint2* cand = (const uint2*)(w + a.cand_off);
+  for (uint32_t i = tid; i < nc; i += FIN_NT) {
+    const uint32_t key = cand[i].x;
+    if (((key >> 10) & 0x7FFu) == b2) atomicAdd(&hist3[key & 0x3FFu], 1u);
+  }
+  __syncthreads();
+  find_digit<FIN_NT, 1024>(hist3, rem2, sh, b3, rem3);
+  const uint32_t T = (b1 << 21) | (b2 << 10) | b3;
+  const uint32_t need = rem3;                                     // keys == T taken, lowest index first
+  for (uint32_t i = tid; i < nc; i += FIN_NT) {
+    const uint2 c = cand[i];
+    const int ch = (int)(c.y / (uint32_t)a.chunk);
+    if (c.x > T) atomicAdd(&gtx[ch], 1u);
+    else if (c.x == T) atomicAdd(&eqc[ch], 1u);
+  }
+  __syncthreads();
+  // per-chunk prefix: ties before the chunk, then the output offset of the chunk
+  const int nch = (li.n + a.chunk - 1) / a.chunk;
+  const uint32_t my_eq = tid < nch ? eqc[tid] : 0u;
+  uint32_t tot;
+  const uint32_t tb = block_scan_excl<FIN_NT>(my_eq, sh, tot, false);
+  const uint32_t take = tb >= need ? 0u : min(need - tb, my_eq);
+  const uint32_t my_sel = tid < nch ? w[W_CHUNKS + tid] + gtx[tid] + take : 0u;
+  const uint32_t off = block_scan_excl<FIN_NT>(my_sel, sh, tot, false);
+  if (tid < nch) {
+    w[W_CHUNKS + a.max_chunks + tid] = off;                       // output offset of the chunk
+    w[W_CHUNKS + 2 * a.max_chunks + tid] = tb;                    // ties in earlier chunks
+    w[W_CHUNKS + 3 * a.max_chunks + tid] = my_sel;                // selected in the chunk
+  }
+  if (tid == 0) {
+    w[W_T] = T;
+    w[W_NEED] = need;
+  }
+}
+
+__global__ __launch_bounds__(CH_NT) void sel_write_kernel(SelectArgs a) {
+  constexpr int E = 16;                                          // consecutive elements per thread
+  const int list = blockIdx.y;
+  const ListInfo li = list_info(a, list);
+  const int c0 = blockIdx.x * a.chunk;
+  if (li.kk == 0 || c0 >= li.n) return;
+  const int c1 = min(li.n, c0 + a.chunk);
+  int32_t* out = a.sel_idx + (size_t)list * a.cap;
+  if (li.kk >= li.n) {                                           // every candidate selected
+    for (int j = c0 + threadIdx.x; j < c1; j += CH_NT) out[j] = j;
+    return;
+  }
+  const uint32_t* w = ws_list(a, list);
+  const int ch = blockIdx.x;
+  const uint32_t nsel = w[W_CHUNKS + 3 * a.max_chunks + ch];
+  if (nsel == 0u) return;
+  const uint32_t T = w[W_T], need = w[W_NEED];
+  uint32_t pos_base = w[W_CHUNKS + a.max_chunks + ch];
+  uint32_t ties = w[W_CHUNKS + 2 * a.max_chunks + ch];
+  __shared__ float stage[E * CH_NT];
+  __shared__ uint32_t sh[3 * (CH_NT / 64) + 3];
+  const float* s = a.scores + (size_t)list * a.s_stride;
+  for (int p0 = c0; p0 < c1; p0 += E * CH_NT) {
+    const int pn = min(E * CH_NT, c1 - p0);
+    for (int i = threadIdx.x; i < pn; i += CH_NT) stage[i] = s[p0 + i];
+    __syncthreads();
+    uint32_t gt = 0u, eq = 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = threadIdx.x * E + e;
+      if (i < pn) {
+        const uint32_t key = f32_key(stage[i]);
+        gt |= (key > T ? 1u : 0u) << e;
+        eq |= (key == T ? 1u : 0u) << e;
+      }
+    }
+    uint32_t tot_eq, tot_sel;
+    uint32_t r = ties + block_scan_excl<CH_NT>(__builtin_popcount(eq), sh, tot_eq, false);
+    uint32_t sel = gt;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if ((eq >> e) & 1u) {
+        if (r < need) sel |= 1u << e;
+        ++r;
+      }
+    uint32_t pos = pos_base + block_scan_excl<CH_NT>(__builtin_popcount(sel), sh, tot_sel, false);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if ((sel >> e) & 1u) {
+        if (pos < (uint32_t)li.kk) out[pos] = p0 + threadIdx.x * E + e;
+        ++pos;
+      }
+    pos_base += tot_sel;
+    ties += tot_eq;
+  }
+}
+
+static_assert(W_ZERO == SELECT_ZERO_WORDS, "cleared words of the selection workspace");
+
+hipError_t launch_select(const SelectArgs& a, int n_lists, bool fused_prefix, hipStream_t st) {
+  const dim3 g(a.max_chunks, n_lists);
+  if (!fused_prefix) {
+    hipLaunchKernelGGL(sel_zero_kernel, dim3(n_lists), dim3(CH_NT), 0, st, a);
+    hipLaunchKernelGGL(sel_hist1_kernel, g, dim3(CH_NT), 0, st, a);
+  }
+  hipLaunchKernelGGL(sel_cand_kernel, g, dim3(CH_NT), 0, st, a);
+  hipLaunchKernelGGL(sel_finalize_kernel, dim3(n_lists), dim3(FIN_NT), 0, st, a);
+  hipLaunchKernelGGL(sel_write_kernel, g, dim3(CH_NT), 0, st, a);
   return hipGetLastError();
+}
+
+// Chunking and workspace layout of the selection, shared with the host planner.
+void select_plan(int64_t s_stride, SelectPlan& p) {
+  p.chunk = 4096;
+  while ((s_stride + p.chunk - 1) / p.chunk > 1024) p.chunk *= 2;  // finalize handles <= 1024 chunks
+  p.max_chunks = (int)std::max<int64_t>(1, (s_stride + p.chunk - 1) / p.chunk);
+  p.cand_off = (W_CHUNKS + 4 * (int64_t)p.max_chunks + 1) & ~(int64_t)1;   // 8-byte aligned pairs
+  p.ws_stride = p.cand_off + 2 * std::max<int64_t>(s_stride, 1);
 }
 
 }  // namespace hs

@@ -1,0 +1,459 @@
+// Decode kernels for at most 32 query rows per KV head (the MQA decode shapes:
+// 32 heads x 1 query token, 16 heads x 2, 8 heads x 4), bf16 or FP8 caches.
+//
+// Every wave streams its own 32-token tiles with no workgroup barrier in the
+// loop, so a CU keeps many independent tiles in flight from HBM.
+//
+//  attn_wave    full layer (dense, all L_b rows) or sparse layer (gather: the
+//               rows of a selection list).  ithome page "小米公开 MiMo-V3 核心架构
+//               HySparse2", section "KV Reuse": the sparse layers read the full
+//               layer's cache at the positions it selected.  A workgroup whose
+//               chunk is the whole list writes O (and LSE) itself; otherwise it
+//               writes one (m, l, acc) partial and attn_merge combines them.
+//  scores_wave  second pass of the full layer: s_j = sum over the heads of a
+//               group of exp(l_j - LSE) for the candidates outside the recent
+//               window (ithome page, "KV Reuse" and recent-window paragraphs),
+//               plus the first-digit histogram the selection starts from.
+
+#include "hs_common.hpp"
+#include "hs_internal.hpp"
+#include "hs_mfma.hpp"
+
+namespace hs {
+
+namespace {
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Clears a strided set of words (caller-specified) with the whole grid.
+__device__ __forceinline__ void zero_hook(const AttnArgs& a) {
+  if (!a.zero_ptr) return;
+  const int64_t total = (int64_t)a.zero_lists * a.zero_words;
+  const int64_t nwg = (int64_t)gridDim.x * gridDim.y;
+  const int64_t wg = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  for (int64_t i = wg * blockDim.x + threadIdx.x; i < total; i += nwg * blockDim.x)
+    a.zero_ptr[(i / a.zero_words) * a.zero_stride + (i % a.zero_words)] = 0u;
+}
+
+}  // namespace
+
+template <int KVT, int NW, bool GATHER>
+__global__ __launch_bounds__(64 * NW) void attn_wave_kernel(AttnArgs a) {
+  constexpr int NT = 64 * NW;
+  using M = Mma<CT_BF16>;
+  constexpr int ROWB = M::ROWB;
+  constexpr bool FP8 = KVT == KV_FP8;
+  constexpr bool SPLIT = KVT != KV_FP8;
+  constexpr int SB = (KVT == KV_BF16 ? 2 : 1) * D;               // storage bytes per row
+  constexpr int PPR = SB / 16;                                   // 16-byte pieces per row
+  constexpr int PPL = 32 * PPR / 64;                             // pieces per lane per tensor
+  constexpr int MAXG = 1152;
+  constexpr int TILES = NW * 2 * 32 * ROWB;
+  constexpr int MERGE = NW * 32 * (D + 2) * 4;
+  __shared__ __align__(16) char smem[TILES > MERGE ? TILES : MERGE];
+  __shared__ __align__(16) char qs[32 * ROWB];
+  __shared__ float ksc[FP8 ? NW * 32 : 1], vsc[FP8 ? NW * 32 : 1];
+  __shared__ int gidx[GATHER ? MAXG + 32 : 1];
+
+  zero_hook(a);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int list = blockIdx.y, chunk = blockIdx.x;
+  int b, t0, g;
+  if (GATHER) { g = list % a.n_kv; const int bt = list / a.n_kv; b = bt / a.n_q; t0 = bt % a.n_q; }
+  else { g = list % a.n_kv; b = list / a.n_kv; t0 = 0; }
+  const int Lb = a.seq_len[b];
+  const int ntok = GATHER ? min(max(a.sel_count[(size_t)list], 0), a.sel_cap) : Lb;
+  const int c0 = chunk * a.chunk;
+  if (c0 >= ntok) return;
+  const int c1 = min(ntok, c0 + a.chunk);
+  const int64_t rs = a.row_start[b];
+  const char* kbase = (const char*)a.k + ((size_t)rs * a.n_kv + g) * SB;
+  const char* vbase = (const char*)a.v + ((size_t)rs * a.n_kv + g) * SB;
+  const size_t rstride = (size_t)a.n_kv * SB;
+
+  // Q rows -> LDS (row r = tt*G + hh; rows >= R are zero)
+  for (int p = tid; p < 32 * 16; p += NT) {
+    const int r = p >> 4, c = p & 15;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (r < a.R) {
+      const int t = t0 + r / a.G, hh = r % a.G;
+      const size_t qoff = (((size_t)b * a.n_q + t) * a.H + (size_t)g * a.G + hh) * D + c * 8;
+      if (a.q_f32) {
+        const float* qf = (const float*)a.q + qoff;
+        for (int j = 0; j < 4; ++j) x[j] = f32_to_bf16_rne(qf[2 * j]) | (f32_to_bf16_rne(qf[2 * j + 1]) << 16);
+      } else {
+        x = *(const u32x4*)((const uint16_t*)a.q + qoff);
+      }
+    }
+    *(u32x4*)(qs + r * ROWB + c * 16) = x;
+  }
+  if (GATHER) {
+    const int32_t* il = a.sel_idx + (size_t)list * a.sel_cap;
+    for (int i = tid; i < c1 - c0; i += NT) {
+      const int j = il[c0 + i];
+      gidx[i] = (j >= 0 && j < Lb) ? j : -1;
+    }
+  }
+  __syncthreads();
+
+  char* const kt = smem + wave * 2 * 32 * ROWB;
+  char* const vt = kt + 32 * ROWB;
+  float* const wks = FP8 ? ksc + wave * 32 : nullptr;
+  float* const wvs = FP8 ? vsc + wave * 32 : nullptr;
+  const int ntiles = (c1 - c0 + 31) / 32;
+
+  // Cache row of a tile position, clamped into the list so every load stays in bounds and needs no
+  // branch (a branch around a load makes the compiler wait for it at the join); positions past the
+  // chunk and invalid indices are masked in the softmax instead.
+  auto tok_row = [&](int tile, int tok) -> int {
+    const int pos = min(c0 + tile * 32 + tok, c1 - 1);
+    return GATHER ? max(gidx[pos - c0], 0) : pos;
+  };
+  u32x4 rk[PPL], rv[PPL];
+  float sk = 0.f, sv = 0.f;
+  auto load = [&](int tile) {
+#pragma unroll
+    for (int i = 0; i < PPL; ++i) {
+      const int p = lane + 64 * i, tok = p / PPR, c = p % PPR;
+      const size_t off = (size_t)tok_row(tile, tok) * rstride + c * 16;
+      rk[i] = *(const u32x4*)(kbase + off);
+      rv[i] = *(const u32x4*)(vbase + off);
+    }
+    if (FP8) {
+      const size_t r = (size_t)rs + tok_row(tile, lane & 31);
+      sk = a.k_scale[r * a.n_kv + g];
+      sv = a.v_scale[r * a.n_kv + g];
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < PPL; ++i) {
+      const int p = lane + 64 * i, tok = p / PPR, c = p % PPR;
+      if constexpr (FP8) {                                       // 16 codes -> 16 bf16 (exact)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const u32x4 x = t2 ? rv[i] : rk[i];
+          char* dst = (t2 ? vt : kt) + tok * ROWB + c * 32;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            u32x4 o;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const uint32_t word = x[2 * h + (w >> 1)];
+              const uint32_t c0b = (word >> (16 * (w & 1))) & 0xFFu, c1b = (word >> (16 * (w & 1) + 8)) & 0xFFu;
+              o[w] = (__float_as_uint(e4m3_to_f32(c0b)) >> 16) | (__float_as_uint(e4m3_to_f32(c1b)) & 0xFFFF0000u);
+            }
+            *(u32x4*)(dst + 16 * h) = o;
+          }
+        }
+      } else {
+        *(u32x4*)(kt + tok * ROWB + c * 16) = rk[i];
+        *(u32x4*)(vt + tok * ROWB + c * 16) = rv[i];
+      }
+    }
+    if (FP8 && lane < 32) { wks[lane] = sk; wvs[lane] = sv; }   // masked tokens get p = 0 below
+  };
+
+  float m = -INFINITY, lsum = 0.f;
+  f32x16 acc[4] = {};
+  const float sl2 = a.scale_log2;
+  if (wave < ntiles) load(wave);
+  for (int tile = wave; tile < ntiles; tile += NW) {
+    wave_sync();
+    store();
+    wave_sync();
+    if (tile + NW < ntiles) load(tile + NW);
+    f32x16 s = {};                                               // S^T = K Q^T, Q operand from LDS
+    {
+      const char* kb = kt + (lane & 31) * ROWB + (lane >> 5) * 16;
+      const char* qb = qs + (lane & 31) * ROWB + (lane >> 5) * 16;
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const s16x8 ka = *(const s16x8*)(kb + 32 * st);
+        const s16x8 qa = *(const s16x8*)(qb + 32 * st);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka), __builtin_bit_cast(bf16x8, qa), s,
+                                                    0, 0, 0);
+      }
+    }
+    float l2[16];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tk = crow(lane, r);
+      const int pos = c0 + tile * 32 + tk;
+      bool ok = pos < c1;
+      if (GATHER) ok = ok && gidx[pos - c0] >= 0;
+      float x = s[r] * sl2;
+      if (FP8) x *= wks[tk];
+      l2[r] = ok ? x : -INFINITY;
+      mt = fmaxf(mt, l2[r]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = fmaxf(m, mt);
+    const float msub = mn == -INFINITY ? 0.f : mn;
+    const float alpha = exp2f(m - msub);
+    float p[16];
+    lsum *= alpha;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p[r] = exp2f(l2[r] - msub);
+      lsum += p[r];
+      if (FP8) p[r] *= wvs[crow(lane, r)];
+    }
+    m = mn;
+#pragma unroll
+    for (int mt4 = 0; mt4 < 4; ++mt4) acc[mt4] *= alpha;
+    M::template pv<SPLIT>(acc, vt, p, lane);
+  }
+  lsum += __shfl_xor(lsum, 32);
+
+  // merge the NW waves (fixed order) through LDS
+  __syncthreads();
+  float* accb = (float*)smem;                                     // [wave][32 rows][128]
+  float* mlb = accb + NW * 32 * D;                                // [wave][32][2]
+  {
+    float* mine = accb + (wave * 32 + (lane & 31)) * D;
+#pragma unroll
+    for (int mt4 = 0; mt4 < 4; ++mt4)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 o = {acc[mt4][4 * r4], acc[mt4][4 * r4 + 1], acc[mt4][4 * r4 + 2], acc[mt4][4 * r4 + 3]};
+        *(f32x4*)(mine + 32 * mt4 + crow(lane, 4 * r4)) = o;
+      }
+    if (lane < 32) {
+      mlb[(wave * 32 + lane) * 2] = m;
+      mlb[(wave * 32 + lane) * 2 + 1] = lsum;
+    }
+  }
+  __syncthreads();
+  constexpr int PER = 32 * D / NT;                                // d values per thread
+  const int lin = tid * PER, row = lin / D, d0 = lin % D;
+  const bool row_ok = row < a.R;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NW; ++j) mx = fmaxf(mx, mlb[(j * 32 + row) * 2]);
+  const float msub = mx == -INFINITY ? 0.f : mx;
+  float ls = 0.f;
+  f32x4 o[PER / 4];
+#pragma unroll
+  for (int e = 0; e < PER / 4; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    const float wj = exp2f(mlb[(j * 32 + row) * 2] - msub);
+    ls += wj * mlb[(j * 32 + row) * 2 + 1];
+#pragma unroll
+    for (int e = 0; e < PER / 4; ++e) o[e] += wj * *(const f32x4*)(accb + (j * 32 + row) * D + d0 + 4 * e);
+  }
+  const int t = t0 + (row_ok ? row / a.G : 0), hh = row_ok ? row % a.G : 0;
+  const size_t orow = ((size_t)b * a.n_q + t) * a.H + (size_t)g * a.G + hh;
+  if (a.direct) {                                                 // one chunk per list: final output
+    if (row_ok) {
+      const float inv = ls > 0.f ? 1.f / ls : 0.f;
+#pragma unroll
+      for (int e = 0; e < PER / 4; ++e) *(f32x4*)(a.out + orow * D + d0 + 4 * e) = o[e] * inv;
+      if (d0 == 0) {
+        const float l2v = ls > 0.f ? mx + __log2f(ls) : -INFINITY;
+        if (a.lse) a.lse[orow] = l2v * LN2;
+        if (a.lse2) a.lse2[orow] = l2v;
+      }
+    }
+    return;
+  }
+  const size_t base = (size_t)list * a.max_chunks;
+  if (row_ok) {
+    float* pa = a.part_acc + ((base + chunk) * a.R + row) * D + d0;
+#pragma unroll
+    for (int e = 0; e < PER / 4; ++e) *(f32x4*)(pa + 4 * e) = o[e];
+    if (d0 == 0) *(float2*)(a.part_ml + ((base + chunk) * a.R + row) * 2) = make_float2(mx, ls);
+  }
+}
+
+// Score pass: each wave streams 64-token K tiles (coalesced 1 KB loads) with
+// one tile prefetched in registers while the previous one, staged in the
+// wave's own LDS slice, feeds the MFMA B operand (S = Q K^T: lane = token, 16
+// rows per lane), so the sum over a query token's heads is mostly in-lane.
+template <int KVT, int NW, int NQ>
+__global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
+  constexpr bool FP8 = KVT == KV_FP8;
+  constexpr int NT = 64 * NW;
+  constexpr int TT = 64;                                         // tokens per wave tile
+  constexpr int ROWB = 272;                                      // bf16 row + 16-byte pad
+  constexpr int SB = (KVT == KV_BF16 ? 2 : 1) * D;
+  constexpr int PPR = SB / 16;
+  constexpr int PPL = TT * PPR / 64;                             // 16-byte pieces per lane per tile
+  __shared__ uint32_t hist[NQ][2048];
+  __shared__ __align__(16) char qs[32 * ROWB];
+  __shared__ __align__(16) char ktile[NW][TT * ROWB];
+  __shared__ float ksc[FP8 ? NW : 1][TT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = blockIdx.y % a.n_kv, b = blockIdx.y / a.n_kv;
+  const int Lb = a.seq_len[b];
+  const int w = min(a.window, Lb);
+  const int ncand = Lb - w;
+  const int c0 = blockIdx.x * a.chunk;
+  if (c0 >= ncand) return;
+  const int c1 = min(ncand, c0 + a.chunk);
+  const bool do_hist = a.hist != nullptr;
+  if (do_hist)
+    for (int i = tid; i < NQ * 2048; i += NT) hist[i >> 11][i & 2047] = 0u;
+  for (int p = tid; p < 32 * 16; p += NT) {
+    const int r = p >> 4, c = p & 15;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (r < a.R) {
+      const size_t qoff = (((size_t)b * a.n_q + r / a.G) * a.H + (size_t)g * a.G + r % a.G) * D + c * 8;
+      if (a.q_f32) {
+        const float* qf = (const float*)a.q + qoff;
+        for (int j = 0; j < 4; ++j) x[j] = f32_to_bf16_rne(qf[2 * j]) | (f32_to_bf16_rne(qf[2 * j + 1]) << 16);
+      } else {
+        x = *(const u32x4*)((const uint16_t*)a.q + qoff);
+      }
+    }
+    *(u32x4*)(qs + r * ROWB + c * 16) = x;
+  }
+  __syncthreads();
+  s16x8 qop[8];                                                  // A = Q: row (l & 31), d = 16 s + 8 (l >> 5)
+#pragma unroll
+  for (int s = 0; s < 8; ++s) qop[s] = *(const s16x8*)(qs + (lane & 31) * ROWB + (16 * s + 8 * (lane >> 5)) * 2);
+  float lse2[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {                                 // rows past R: p = exp2(-inf) = 0
+    const int rw = crow(lane, r), rc = min(rw, a.R - 1);
+    const float v = a.lse2[((size_t)b * a.n_q + rc / a.G) * a.H + (size_t)g * a.G + rc % a.G];
+    lse2[r] = rw < a.R ? v : INFINITY;
+  }
+  const int64_t rs = a.row_start[b];
+  const char* kbase = (const char*)a.k + ((size_t)rs * a.n_kv + g) * SB;
+  const size_t rstride = (size_t)a.n_kv * SB;
+  const int ntiles = (c1 - c0 + TT - 1) / TT;
+  char* const kt = ktile[wave];
+  u32x4 kr[PPL];
+  float ks = 0.f;
+  auto load = [&](int tile) {                                    // clamped rows: no branch, in bounds
+#pragma unroll
+    for (int i = 0; i < PPL; ++i) {
+      const int p = lane + 64 * i;
+      const int pos = min(c0 + tile * TT + p / PPR, c1 - 1);
+      kr[i] = *(const u32x4*)(kbase + (size_t)pos * rstride + (p % PPR) * 16);
+    }
+    if (FP8) ks = a.k_scale[((size_t)rs + min(c0 + tile * TT + lane, c1 - 1)) * a.n_kv + g];
+  };
+  const int tpw = a.G >= 32 ? 1 : 32 / a.G;                      // query tokens in the 32 rows
+  float* sout = a.scores + (size_t)b * a.n_q * a.n_kv * a.s_stride;
+  if (wave < ntiles) load(wave);
+  for (int tile = wave; tile < ntiles; tile += NW) {
+    wave_sync();
+#pragma unroll
+    for (int i = 0; i < PPL; ++i) {                              // registers -> LDS (FP8 -> bf16)
+      const int p = lane + 64 * i, tok = p / PPR, c = p % PPR;
+      const u32x4 x = kr[i];
+      if constexpr (FP8) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          u32x4 o;
+#pragma unroll
+          for (int ww = 0; ww < 4; ++ww) {
+            const uint32_t word = x[2 * h + (ww >> 1)];
+            const uint32_t c0b = (word >> (16 * (ww & 1))) & 0xFFu, c1b = (word >> (16 * (ww & 1) + 8)) & 0xFFu;
+            o[ww] = (__float_as_uint(e4m3_to_f32(c0b)) >> 16) | (__float_as_uint(e4m3_to_f32(c1b)) & 0xFFFF0000u);
+          }
+          *(u32x4*)(kt + tok * ROWB + c * 32 + 16 * h) = o;
+        }
+      } else {
+        *(u32x4*)(kt + tok * ROWB + c * 16) = x;
+      }
+    }
+    if (FP8) ksc[wave][lane] = ks;
+    wave_sync();
+    if (tile + NW < ntiles) load(tile + NW);                     // in flight during the two sub-tiles
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      f32x16 s = {};
+      const char* kb = kt + (32 * half + (lane & 31)) * ROWB + (lane >> 5) * 16;
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const s16x8 kv = *(const s16x8*)(kb + 32 * st);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qop[st]), __builtin_bit_cast(bf16x8, kv),
+                                                    s, 0, 0, 0);
+      }
+      const float f = a.scale_log2 * (FP8 ? ksc[wave][32 * half + (lane & 31)] : 1.f);
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[r] = exp2f(s[r] * f - lse2[r]);
+      const int pos = c0 + tile * TT + 32 * half + (lane & 31);
+      float tv[NQ];
+      if (tpw == 1) {
+        float v = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v += p[r];
+        tv[0] = v + __shfl_xor(v, 32);
+      } else {
+        float blk[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          blk[q4] = p[4 * q4] + p[4 * q4 + 1] + p[4 * q4 + 2] + p[4 * q4 + 3];
+          blk[q4] += __shfl_xor(blk[q4], 32);
+        }
+#pragma unroll
+        for (int t = 0; t < NQ; ++t) tv[t] = tpw == 4 ? blk[t] : blk[2 * t] + blk[2 * t + 1];
+      }
+      if (lane < 32 && pos < c1) {
+#pragma unroll
+        for (int t = 0; t < NQ; ++t) {
+          if (t >= a.n_q) break;
+          sout[((size_t)t * a.n_kv + g) * a.s_stride + pos] = tv[t];
+          if (do_hist) atomicAdd(&hist[t][f32_key(tv[t]) >> 21], 1u);
+        }
+      }
+    }
+  }
+  if (!do_hist) return;
+  __syncthreads();
+  for (int i = tid; i < a.n_q * 2048; i += NT) {
+    const uint32_t v = hist[i >> 11][i & 2047];
+    if (v) atomicAdd(a.hist + (((size_t)b * a.n_q + (i >> 11)) * a.n_kv + g) * a.hist_stride + (i & 2047), v);
+  }
+}
+
+template <int KVT, bool GATHER>
+static hipError_t launch_wave_t(const AttnArgs& a, hipStream_t st) {
+  constexpr int NW = 8;
+  dim3 grid(a.max_chunks, a.n_lists, 1);
+  hipLaunchKernelGGL((attn_wave_kernel<KVT, NW, GATHER>), grid, dim3(64 * NW), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_wave(const AttnArgs& a, int kvt, bool gather, hipStream_t st) {
+  if (a.R > 32) return hipErrorInvalidValue;
+  if (kvt == KV_BF16) return gather ? launch_wave_t<KV_BF16, true>(a, st) : launch_wave_t<KV_BF16, false>(a, st);
+  if (kvt == KV_FP8) return gather ? launch_wave_t<KV_FP8, true>(a, st) : launch_wave_t<KV_FP8, false>(a, st);
+  return hipErrorInvalidValue;
+}
+
+template <int KVT, int NQ>
+static void launch_scores_wave_t(const ScoreArgs& a, hipStream_t st) {
+  constexpr int NW = NQ == 1 ? 8 : 6;                            // LDS: NW x 17 KB tiles + NQ x 8 KB histograms
+  dim3 grid(a.max_chunks, a.n_lists, 1);
+  hipLaunchKernelGGL((scores_wave_kernel<KVT, NW, NQ>), grid, dim3(64 * NW), 0, st, a);
+}
+
+hipError_t launch_scores_wave(const ScoreArgs& a, int kvt, hipStream_t st) {
+  if (a.R > 32 || a.n_q > 4 || (kvt != KV_BF16 && kvt != KV_FP8)) return hipErrorInvalidValue;
+  const int nq = a.n_q == 1 ? 1 : a.n_q == 2 ? 2 : 4;
+  if (kvt == KV_BF16) {
+    if (nq == 1) launch_scores_wave_t<KV_BF16, 1>(a, st);
+    else if (nq == 2) launch_scores_wave_t<KV_BF16, 2>(a, st);
+    else launch_scores_wave_t<KV_BF16, 4>(a, st);
+  } else {
+    if (nq == 1) launch_scores_wave_t<KV_FP8, 1>(a, st);
+    else if (nq == 2) launch_scores_wave_t<KV_FP8, 2>(a, st);
+    else launch_scores_wave_t<KV_FP8, 4>(a, st);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hs

@@ -260,9 +260,10 @@ def select_from_scores(scores, seq_len, q_tokens, n_kv, top_k=1024, window=128, 
     d_seq = torch.from_numpy(h_seq).to(dev)
     sel_idx = torch.empty((B, q_tokens, n_kv, top_k + window), dtype=torch.int32, device=dev)
     sel_count = torch.empty((B, q_tokens, n_kv), dtype=torch.int32, device=dev)
+    ws = workspace(lib.hs_select_workspace_size(B, q_tokens, n_kv, max_len, top_k, window), dev)
     check(lib.hs_select_from_scores(_ptr(scores), _ptr(d_seq), h_seq.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                                     B, q_tokens, n_kv, max_len, top_k, window, _ptr(sel_idx), _ptr(sel_count),
-                                    None, 0, _stream(stream)))
+                                    _ptr(ws), ws.numel(), _stream(stream)))
     return sel_idx, sel_count
 
 
