@@ -29,9 +29,9 @@ METRIC = "hybrid-block decode queries/s + achieved HBM GB/s at 128K–1M ctx, 1 
 # HBM bytes per launch of the dense split-K pass at the default workload, from two
 # rocprofv3 --pmc runs (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors read off a
 # plain 1 GiB copy), keyed by a digest of the kernel sources they were taken on.
-KNOWN_TRAFFIC = {"f9c62c8194e664a8": 2166878208}
-KERNEL_SOURCES = ["long_context_split_amd/csrc/hs_attn.hip", "long_context_split_amd/csrc/hs_common.hpp",
-                  "long_context_split_amd/csrc/hs_internal.hpp"]
+KNOWN_TRAFFIC = {}
+KERNEL_SOURCES = ["long_context_split_amd/csrc/hs_wave.hip", "long_context_split_amd/csrc/hs_mfma.hpp",
+                  "long_context_split_amd/csrc/hs_common.hpp", "long_context_split_amd/csrc/hs_internal.hpp"]
 
 
 def kernel_digest():
@@ -58,7 +58,9 @@ def parse():
     ap.add_argument("--B", type=int, default=None, help="batch override (sweeps)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle time budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-flush", action="store_true", help="skip the Infinity Cache flush between steps")
+    ap.add_argument("--flush", choices=["read", "write", "none"], default="read",
+                    help="evict the 256 MB Infinity Cache between steps by reading (default) or writing 1 GiB")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP-graph replay")
     ap.add_argument("--no-bridge", action="store_true", help="skip the KV Bridging measurement")
     ap.add_argument("--bridge-iters", type=int, default=10)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -125,23 +127,48 @@ def main():
                 hs.sparse_attn(kv, bl["qs"][i], bl["idx"], bl["cnt"], top_k, window, out=bl["so"][i],
                                ws=bl["ws_sp"])
 
-    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush_buf = None if args.flush == "none" else torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
+    flush_sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def flush(i):
+        # evict the 256 MB Infinity Cache between steps (outside the step's events); reading 1 GiB
+        # leaves clean lines, writing leaves dirty ones that drain during the next step
+        if flush_buf is None:
+            return
+        if args.flush == "read":
+            torch.sum(flush_buf, dim=(0,), out=flush_sink)
+        else:
+            flush_buf.fill_(float(i & 0xFF))
 
     # ---------------------------------------------------------------- warmup
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
+    graph = None
+    if not args.eager:
+        side = torch.cuda.Stream()
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        log("step captured in a HIP graph")
 
     # ---------------------------------------------------------------- timed region: step time
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall0 = time.time()
     for i in range(args.steps):
-        if flush is not None:
-            flush.fill_(i & 0xFF)                 # evict the 256 MB Infinity Cache between steps
+        flush(i)
         ev[i][0].record()
-        step()
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
         ev[i][1].record()
     torch.cuda.synchronize()
     wall = time.time() - wall0
@@ -156,8 +183,7 @@ def main():
     hs.timing_collect()
     torch.cuda.synchronize()
     for i in range(args.steps):
-        if flush is not None:
-            flush.fill_(i & 0xFF)
+        flush(i)
         step()
     torch.cuda.synchronize()
     recs = hs.timing_collect()
@@ -187,7 +213,8 @@ def main():
     qps = queries / (ms * 1e-3)
 
     dom = max(kern.items(), key=lambda x: x[1]["total_ms_per_step"])[0] if kern else None
-    k1 = kern.get("attn_partial_dense")
+    k1_name = "attn_wave_dense" if "attn_wave_dense" in kern else "attn_partial_dense"
+    k1 = kern.get(k1_name)
     k1_bytes = sum_L * row_bytes                                 # per launch (one block's full layer)
     roof = None
     if k1:
@@ -195,7 +222,7 @@ def main():
         default_workload = args.config == 2 and args.L is None and args.B is None
         traffic = KNOWN_TRAFFIC.get(kernel_digest()) if default_workload else None
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": "attn_partial_dense",
+                "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": k1_name,
                 "algorithmic_bytes_per_launch": k1_bytes, "avg_launch_us": round(k1["avg_ms"] * 1e3, 2),
                 "dominant_kernel_by_time": dom}
 
@@ -243,8 +270,10 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "bridge": bridge,
-        "timing": "HIP events per step; Infinity Cache flushed between steps" if flush is not None
-        else "HIP events per step; no cache flush",
+        "timing": ("HIP-graph replay of the step" if graph is not None else "eager launches") +
+                  "; HIP events per step" + ("" if args.flush == "none" else
+                                             f"; Infinity Cache flushed between steps by a 1 GiB {args.flush}") +
+                  "; kernel durations from per-launch HIP events on the library stream in a second (eager) region",
     }
     print(json.dumps(line), flush=True)
 

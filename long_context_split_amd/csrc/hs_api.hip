@@ -212,7 +212,7 @@ hs_status plan_full(const hs_kv_cache* kv, const hs_attn_params* p, hs_dtype q_d
 }
 
 struct SparsePlan {
-  int wave;  // 1: attn_wave (G <= 32, bf16/FP8 cache), partials merged by the last workgroup of a list
+  int wave;  // 1: attn_wave (G <= 32, bf16/FP8 cache); several chunks are combined by attn_merge
   int ct, nwr, G, n_lists, chunk, max_chunks, cap;
   size_t off_acc, off_ml, total;
 };
@@ -228,9 +228,10 @@ void plan_sparse(const hs_kv_cache* kv, const hs_attn_params* p, hs_dtype q_dtyp
   const int tt = pl.wave ? 256 : hs::partial_tile_tokens(pl.nwr);   // attn_wave: 8 waves x 32 rows
   const int tiles = (pl.cap + tt - 1) / tt;
   int per_list = std::max(1, std::min(tiles, (512 + pl.n_lists - 1) / pl.n_lists));
+  // attn_wave: 256-row chunks (5 workgroups per 1152-row list) and a merge launch beat one workgroup
+  // per list (the single-chunk direct form) on 32 lists; HS_SPARSE_CHUNK overrides (>= cap: direct)
   int chunk = env_int("HS_SPARSE_CHUNK", 0);
-  if (chunk <= 0) chunk = ((tiles + per_list - 1) / per_list) * tt;
-  if (pl.wave && env_int("HS_SPARSE_CHUNK", 0) <= 0) chunk = pl.cap;   // one workgroup per list, no merge
+  if (chunk <= 0) chunk = pl.wave ? 256 : ((tiles + per_list - 1) / per_list) * tt;
   pl.chunk = std::min((int)align_up((size_t)chunk, (size_t)tt), 1152);
   pl.max_chunks = (pl.cap + pl.chunk - 1) / pl.chunk;
   size_t off = 0;
@@ -360,11 +361,12 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
   m.part_acc = a.part_acc; m.part_ml = a.part_ml; m.seq_len = kv->d_seq_len; m.sel_count = nullptr;
   m.gather = 0; m.n_kv = ci.n_kv; m.H = a.H; m.G = pl.G; m.n_q = a.n_q; m.R = pl.R; m.n_lists = pl.n_lists;
   m.chunk = pl.chunk; m.max_chunks = pl.max_chunks; m.out = out; m.lse = lse; m.lse2 = lse2;
-  if (!a.direct)                                                  // several chunks: merge them
+  const bool fold_merge = pl.wave && !a.direct && pl.max_chunks <= 64;   // scores_wave merges O, writes LSE
+  if (!a.direct && !fold_merge)                                   // several chunks: merge them
     if ((e = timed("attn_merge_dense", s, [&] { return hs::launch_attn_merge(m, s); })) != hipSuccess)
       return hip_fail(e, "full attention merge");
 
-  if (pl.max_chunks_s > 0) {
+  if (pl.max_chunks_s > 0 || fold_merge) {
     hs::ScoreArgs sa{};
     sa.k = kv->k; sa.k_scale = kv->k_scale; sa.row_start = kv->d_row_start; sa.seq_len = kv->d_seq_len;
     sa.q = q; sa.q_f32 = a.q_f32; sa.n_kv = ci.n_kv; sa.H = a.H; sa.G = pl.G; sa.n_q = a.n_q; sa.R = pl.R;
@@ -373,6 +375,10 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
     if (pl.wave) {
       sa.hist = (uint32_t*)(ws + pl.off_sel);
       sa.hist_stride = pl.sel.ws_stride;
+      if (fold_merge) {
+        sa.part_acc = a.part_acc; sa.part_ml = a.part_ml; sa.dchunk = pl.chunk; sa.dmax_chunks = pl.max_chunks;
+        sa.out = out; sa.lse = lse;
+      }
       if ((e = timed("scores_wave", s, [&] { return hs::launch_scores_wave(sa, kvt, s); })) != hipSuccess)
         return hip_fail(e, "selection scores");
     } else if ((e = timed("attn_scores", s, [&] { return hs::launch_attn_scores(sa, kvt, pl.ct, pl.nwr_s, s); })) !=

@@ -296,31 +296,30 @@ __global__ __launch_bounds__(64 * NWR * NWT) void attn_partial_kernel(AttnArgs a
 
 // One thread per (row, d): combines the chunks of a list in increasing order.
 __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
-  const int list = blockIdx.y;
-  const int row = blockIdx.x * 2 + (threadIdx.x >> 7);
-  const int d = threadIdx.x & 127;
-  if (row >= a.R) return;
+  // one workgroup per (row, list): every wave derives the row's LSE, wave w sums chunks w, w + 4, ...
+  __shared__ float2 part[4][64];
+  const int list = blockIdx.y, row = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int b, t, g;
   if (a.gather) { g = list % a.n_kv; const int bt = list / a.n_kv; b = bt / a.n_q; t = bt % a.n_q; }
   else { g = list % a.n_kv; b = list / a.n_kv; t = row / a.G; }
   const int hh = row % a.G;
   const int ntok = a.gather ? min(max(a.sel_count[list], 0), a.sel_cap) : a.seq_len[b];
   const int nch = (ntok + a.chunk - 1) / a.chunk;
-  const size_t base = (size_t)list * a.max_chunks;
-  float mx = -INFINITY;
-  for (int c = 0; c < nch; ++c) mx = fmaxf(mx, a.part_ml[((base + c) * a.R + row) * 2]);
-  const float msub = mx == -INFINITY ? 0.f : mx;
-  float ls = 0.f, o = 0.f;
-  for (int c = 0; c < nch; ++c) {
-    const size_t it = (base + c) * a.R + row;
-    const float w = exp2f(a.part_ml[it * 2] - msub);
-    ls += w * a.part_ml[it * 2 + 1];
-    o += w * a.part_acc[it * D + d];
-  }
+  const size_t first = (size_t)list * a.max_chunks * a.R + row;
+  const float* ml = a.part_ml + first * 2;
+  const float* acc = a.part_acc + first * D;
+  const float l2 = merged_lse2(ml, (size_t)a.R * 2, nch, lane);
+  part[wave][lane] = l2 == -INFINITY ? make_float2(0.f, 0.f)
+                                     : merged_o(ml, (size_t)a.R * 2, acc, (size_t)a.R * D, wave, nch, 4, l2, lane);
+  __syncthreads();
+  if (wave) return;
+  float2 o = part[0][lane];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) { o.x += part[w][lane].x; o.y += part[w][lane].y; }
   const size_t orow = ((size_t)b * a.n_q + t) * a.H + (size_t)g * a.G + hh;
-  a.out[orow * D + d] = ls > 0.f ? o / ls : 0.f;
-  if (d == 0) {
-    const float l2 = ls > 0.f ? mx + __log2f(ls) : -INFINITY;
+  *(float2*)(a.out + orow * D + 2 * lane) = o;
+  if (lane == 0) {
     if (a.lse) a.lse[orow] = l2 * LN2;
     if (a.lse2) a.lse2[orow] = l2;
   }
@@ -496,7 +495,7 @@ hipError_t launch_attn_partial(const AttnArgs& a, int kvt, int ct, int nwr, bool
 }
 
 hipError_t launch_attn_merge(const MergeArgs& m, hipStream_t st) {
-  dim3 grid((m.R + 1) / 2, m.n_lists);
+  dim3 grid(m.R, m.n_lists);
   hipLaunchKernelGGL(attn_merge_kernel, grid, dim3(256), 0, st, m);
   return hipGetLastError();
 }

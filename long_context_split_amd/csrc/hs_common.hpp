@@ -63,4 +63,61 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Split-K partials of one attention row: chunk c holds (m_c, l_c) at ml[c * mstride] (running max in
+// log2 units, sum of 2^(s - m_c)) and acc_c = sum 2^(s - m_c) v at acc[c * astride].
+
+// log2 sum_c 2^m_c l_c over c < nch, by one wave (lanes over chunks, 4 loads per lane in flight);
+// the same value on every lane, -inf when nch == 0 or the sum is zero.
+__device__ inline float merged_lse2(const float* ml, size_t mstride, int nch, int lane) {
+  float mx = -INFINITY, ls = 0.f;
+  for (int c0 = 0; c0 < nch; c0 += 256) {
+    float2 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + 64 * u + lane;
+      v[u] = *(const float2*)(ml + (size_t)min(c, nch - 1) * mstride);   // clamped: in bounds, no branch
+      if (c >= nch) v[u] = make_float2(-INFINITY, 0.f);
+    }
+    const float nm = fmaxf(mx, wave_max(fmaxf(fmaxf(v[0].x, v[1].x), fmaxf(v[2].x, v[3].x))));
+    if (nm == -INFINITY) continue;                                         // uniform over the wave
+    ls *= exp2f(mx - nm);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) ls += exp2f(v[u].x - nm) * v[u].y;
+    mx = nm;
+  }
+  ls = wave_sum(ls);
+  return ls > 0.f ? mx + __log2f(ls) : -INFINITY;
+}
+
+// sum_c 2^(m_c - l2) acc_c over c = c_first, c_first + step, ... < nch (l2 finite), lanes holding
+// d = 2 lane and 2 lane + 1; 8 chunks in flight.
+__device__ inline float2 merged_o(const float* ml, size_t mstride, const float* acc, size_t astride, int c_first,
+                                  int nch, int step, float l2, int lane) {
+  float2 o = make_float2(0.f, 0.f);
+  for (int c0 = c_first; c0 < nch; c0 += 8 * step) {
+    float m[8];
+    float2 x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = c0 + u * step, cc = min(c, nch - 1);
+      m[u] = ml[(size_t)cc * mstride];
+      x[u] = *(const float2*)(acc + (size_t)cc * astride + 2 * lane);
+      if (c >= nch) m[u] = -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float w = exp2f(m[u] - l2);
+      o.x += w * x[u].x;
+      o.y += w * x[u].y;
+    }
+  }
+  return o;
+}
+
 }  // namespace hs

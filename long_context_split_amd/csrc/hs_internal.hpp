@@ -66,6 +66,13 @@ struct ScoreArgs {
   int64_t s_stride;
   uint32_t* hist;        // scores_wave: first-digit histograms of the selection (nullable),
   int64_t hist_stride;   //   2048 words per list, hist_stride words apart
+  // scores_wave, optional: the full layer's chunk partials (as attn_wave writes them); when set,
+  // the kernel derives LSE from them itself and its workgroups also merge O and write out / lse
+  const float* part_acc;
+  const float* part_ml;
+  int dchunk, dmax_chunks;
+  float* out;
+  float* lse;            // nullable, natural log
 };
 
 struct SelectArgs {

@@ -15,6 +15,8 @@
 //               window (ithome page, "KV Reuse" and recent-window paragraphs),
 //               plus the first-digit histogram the selection starts from.
 
+#include <algorithm>
+
 #include "hs_common.hpp"
 #include "hs_internal.hpp"
 #include "hs_mfma.hpp"
@@ -290,12 +292,34 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
   __shared__ __align__(16) char ktile[NW][TT * ROWB];
   __shared__ float ksc[FP8 ? NW : 1][TT];
 
+  __shared__ float s_lse2[32];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = blockIdx.y % a.n_kv, b = blockIdx.y / a.n_kv;
+  const int list = blockIdx.y;
+  const int g = list % a.n_kv, b = list / a.n_kv;
   const int Lb = a.seq_len[b];
   const int w = min(a.window, Lb);
   const int ncand = Lb - w;
   const int c0 = blockIdx.x * a.chunk;
+  if (a.part_ml) {
+    // The full layer's merge, folded in (at most 64 chunks): every workgroup derives the LSE of all rows
+    // from the chunk partials; row r's output is merged by workgroup r % nwg of the list's nwg >= 1.
+    const int nchd = (Lb + a.dchunk - 1) / a.dchunk;
+    const int nwg = max(1, (ncand + a.chunk - 1) / a.chunk);
+    if ((int)blockIdx.x >= nwg) return;
+    const size_t first = (size_t)list * a.dmax_chunks * a.R;
+    for (int r = wave; r < a.R; r += NW) {
+      const float* ml = a.part_ml + (first + r) * 2;
+      const float l2 = merged_lse2(ml, (size_t)a.R * 2, nchd, lane);
+      if (lane == 0) s_lse2[r] = l2;
+      if (r % nwg != (int)blockIdx.x) continue;
+      const float2 o = l2 == -INFINITY ? make_float2(0.f, 0.f)
+                                       : merged_o(ml, (size_t)a.R * 2, a.part_acc + (first + r) * D, (size_t)a.R * D,
+                                                  0, nchd, 1, l2, lane);
+      const size_t orow = ((size_t)b * a.n_q + r / a.G) * a.H + (size_t)g * a.G + r % a.G;
+      *(float2*)(a.out + orow * D + 2 * lane) = o;
+      if (lane == 0 && a.lse) a.lse[orow] = l2 * LN2;
+    }
+  }
   if (c0 >= ncand) return;
   const int c1 = min(ncand, c0 + a.chunk);
   const bool do_hist = a.hist != nullptr;
@@ -323,7 +347,7 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) {                                 // rows past R: p = exp2(-inf) = 0
     const int rw = crow(lane, r), rc = min(rw, a.R - 1);
-    const float v = a.lse2[((size_t)b * a.n_q + rc / a.G) * a.H + (size_t)g * a.G + rc % a.G];
+    const float v = a.part_ml ? s_lse2[rc] : a.lse2[((size_t)b * a.n_q + rc / a.G) * a.H + (size_t)g * a.G + rc % a.G];
     lse2[r] = rw < a.R ? v : INFINITY;
   }
   const int64_t rs = a.row_start[b];
@@ -437,7 +461,7 @@ hipError_t launch_attn_wave(const AttnArgs& a, int kvt, bool gather, hipStream_t
 template <int KVT, int NQ>
 static void launch_scores_wave_t(const ScoreArgs& a, hipStream_t st) {
   constexpr int NW = NQ == 1 ? 8 : 6;                            // LDS: NW x 17 KB tiles + NQ x 8 KB histograms
-  dim3 grid(a.max_chunks, a.n_lists, 1);
+  dim3 grid(a.part_ml ? std::max(a.max_chunks, 1) : a.max_chunks, a.n_lists, 1);
   hipLaunchKernelGGL((scores_wave_kernel<KVT, NW, NQ>), grid, dim3(64 * NW), 0, st, a);
 }
 

@@ -94,14 +94,18 @@ def test_config1_fp32_full_size():
           f"recall {stats['hit'] / stats['tot']:.6f}", flush=True)
 
 
-@pytest.mark.parametrize("split", [0, 512, 4096])
-def test_ragged_bf16_edge_lengths(split, monkeypatch):
+@pytest.mark.parametrize("split,schunk", [(0, 0), (512, 1152), (4096, 512), (256, 0)])
+def test_ragged_bf16_edge_lengths(split, schunk, monkeypatch):
     """Lengths below, at and around the window and the 1152 capacity, plus several tiles
-    and ragged tails; the split size changes the number of partials merged."""
+    and ragged tails.  The full layer's split size changes the number of partials merged
+    (256: 79 chunks, merged by the separate merge kernel; otherwise at most 64, merged
+    inside the score kernel); the sparse chunk 1152 is the single-workgroup direct form."""
     if split:
         monkeypatch.setenv("HS_SPLIT_TOKENS", str(split))
+    if schunk:
+        monkeypatch.setenv("HS_SPARSE_CHUNK", str(schunk))
     lens = [1, 100, 128, 129, 300, 1152, 1153, 4099, 20000]
-    banner(f"ragged bf16 lens={lens} split={split}")
+    banner(f"ragged bf16 lens={lens} split={split} sparse chunk={schunk}")
     case = synth.decode_case(2, B=len(lens), lengths=lens)
     up = Uploaded(case)
     res = _run_block(up)
