@@ -192,7 +192,7 @@ hs_status plan_full(const hs_kv_cache* kv, const hs_attn_params* p, hs_dtype q_d
   int maxc = 0;
   for (int b = 0; b < ci.B; ++b) maxc = std::max(maxc, kv->h_seq_len[b] - std::min(p->window, kv->h_seq_len[b]));
   pl.s_stride = maxc;
-  pl.chunk_s = pl.chunk;
+  pl.chunk_s = env_int("HS_SCORE_CHUNK", 0) > 0 ? (int)align_up((size_t)env_int("HS_SCORE_CHUNK", 0), 256) : pl.chunk;
   pl.max_chunks_s = (maxc + pl.chunk_s - 1) / pl.chunk_s;
 
   size_t off = 0;
@@ -225,7 +225,7 @@ void plan_sparse(const hs_kv_cache* kv, const hs_attn_params* p, hs_dtype q_dtyp
   pl.n_lists = ci.B * p->q_tokens * ci.n_kv;
   pl.cap = p->top_k + p->window;
   pl.wave = pl.ct == hs::CT_BF16 && pl.G <= 32;
-  const int tt = pl.wave ? 256 : hs::partial_tile_tokens(pl.nwr);   // attn_wave: 8 waves x 32 rows
+  const int tt = pl.wave ? 32 : hs::partial_tile_tokens(pl.nwr);    // attn_wave: 32-row wave tiles
   const int tiles = (pl.cap + tt - 1) / tt;
   int per_list = std::max(1, std::min(tiles, (512 + pl.n_lists - 1) / pl.n_lists));
   // attn_wave: 256-row chunks (5 workgroups per 1152-row list) and a merge launch beat one workgroup

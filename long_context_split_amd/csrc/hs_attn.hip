@@ -296,8 +296,10 @@ __global__ __launch_bounds__(64 * NWR * NWT) void attn_partial_kernel(AttnArgs a
 
 // One thread per (row, d): combines the chunks of a list in increasing order.
 __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
-  // one workgroup per (row, list): every wave derives the row's LSE, wave w sums chunks w, w + 4, ...
-  __shared__ float2 part[4][64];
+  // one workgroup per (row, list): wave w combines chunks w, w + 4, ... in one online pass, then
+  // wave 0 combines the four (m, l, o) in a fixed order
+  __shared__ float2 po[4][64];
+  __shared__ float pm[4], pl[4];
   const int list = blockIdx.y, row = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int b, t, g;
@@ -307,19 +309,28 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
   const int ntok = a.gather ? min(max(a.sel_count[list], 0), a.sel_cap) : a.seq_len[b];
   const int nch = (ntok + a.chunk - 1) / a.chunk;
   const size_t first = (size_t)list * a.max_chunks * a.R + row;
-  const float* ml = a.part_ml + first * 2;
-  const float* acc = a.part_acc + first * D;
-  const float l2 = merged_lse2(ml, (size_t)a.R * 2, nch, lane);
-  part[wave][lane] = l2 == -INFINITY ? make_float2(0.f, 0.f)
-                                     : merged_o(ml, (size_t)a.R * 2, acc, (size_t)a.R * D, wave, nch, 4, l2, lane);
+  const MergePart r = merge_part_wave(a.part_ml + first * 2, (size_t)a.R * 2, a.part_acc + first * D,
+                                      (size_t)a.R * D, wave, nch, 4, lane);
+  po[wave][lane] = r.o;
+  if (lane == 0) { pm[wave] = r.m; pl[wave] = r.l; }
   __syncthreads();
   if (wave) return;
-  float2 o = part[0][lane];
+  const float mx = fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3]));
+  const float msub = mx == -INFINITY ? 0.f : mx;
+  float ls = 0.f;
+  float2 o = make_float2(0.f, 0.f);
 #pragma unroll
-  for (int w = 1; w < 4; ++w) { o.x += part[w][lane].x; o.y += part[w][lane].y; }
+  for (int w = 0; w < 4; ++w) {
+    const float wt = exp2f(pm[w] - msub);
+    ls += wt * pl[w];
+    o.x += wt * po[w][lane].x;
+    o.y += wt * po[w][lane].y;
+  }
+  const float inv = ls > 0.f ? 1.f / ls : 0.f;
   const size_t orow = ((size_t)b * a.n_q + t) * a.H + (size_t)g * a.G + hh;
-  *(float2*)(a.out + orow * D + 2 * lane) = o;
+  *(float2*)(a.out + orow * D + 2 * lane) = make_float2(o.x * inv, o.y * inv);
   if (lane == 0) {
+    const float l2 = ls > 0.f ? mx + __log2f(ls) : -INFINITY;
     if (a.lse) a.lse[orow] = l2 * LN2;
     if (a.lse2) a.lse2[orow] = l2;
   }

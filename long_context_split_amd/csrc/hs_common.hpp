@@ -95,6 +95,46 @@ __device__ inline float merged_lse2(const float* ml, size_t mstride, int nch, in
   return ls > 0.f ? mx + __log2f(ls) : -INFINITY;
 }
 
+// One wave's share of a row's partials, chunks c = c_first, c_first + step, ... < nch, combined in a
+// single online pass (8 chunks in flight): running max m, l and o relative to it (lanes holding
+// d = 2 lane, 2 lane + 1).  m = -inf if the wave had no chunk.  m and l are the same on every lane.
+struct MergePart {
+  float m, l;
+  float2 o;
+};
+
+__device__ inline MergePart merge_part_wave(const float* ml, size_t mstride, const float* acc, size_t astride,
+                                            int c_first, int nch, int step, int lane) {
+  MergePart r{-INFINITY, 0.f, make_float2(0.f, 0.f)};
+  for (int c0 = c_first; c0 < nch; c0 += 8 * step) {
+    float2 q[8], x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = c0 + u * step, cc = min(c, nch - 1);
+      q[u] = *(const float2*)(ml + (size_t)cc * mstride);
+      x[u] = *(const float2*)(acc + (size_t)cc * astride + 2 * lane);
+      if (c >= nch) q[u] = make_float2(-INFINITY, 0.f);
+    }
+    float nm = r.m;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) nm = fmaxf(nm, q[u].x);
+    if (nm == -INFINITY) continue;
+    const float al = exp2f(r.m - nm);
+    r.l *= al;
+    r.o.x *= al;
+    r.o.y *= al;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float w = exp2f(q[u].x - nm);
+      r.l += w * q[u].y;
+      r.o.x += w * x[u].x;
+      r.o.y += w * x[u].y;
+    }
+    r.m = nm;
+  }
+  return r;
+}
+
 // sum_c 2^(m_c - l2) acc_c over c = c_first, c_first + step, ... < nch (l2 finite), lanes holding
 // d = 2 lane and 2 lane + 1; 8 chunks in flight.
 __device__ inline float2 merged_o(const float* ml, size_t mstride, const float* acc, size_t astride, int c_first,

@@ -140,6 +140,7 @@ __global__ __launch_bounds__(CH_NT) void sel_hist1_kernel(SelectArgs a) {
 }
 
 __global__ __launch_bounds__(CH_NT) void sel_cand_kernel(SelectArgs a) {
+  constexpr int PER = 16;                                        // scores per thread per batch
   const int list = blockIdx.y;
   const ListInfo li = list_info(a, list);
   if (li.kk == 0 || li.kk >= li.n) return;
@@ -148,42 +149,53 @@ __global__ __launch_bounds__(CH_NT) void sel_cand_kernel(SelectArgs a) {
   const int c1 = min(li.n, c0 + a.chunk);
   __shared__ uint32_t sh[3 * (CH_NT / 64) + 3];
   __shared__ uint32_t hist2[2048];
+  __shared__ uint32_t s_base;
+  const int tid = threadIdx.x;
+  const float* s = a.scores + (size_t)list * a.s_stride;
+  float v[PER];
+  auto load = [&](int j0) {                                      // clamped: in bounds, no branch
+#pragma unroll
+    for (int e = 0; e < PER; ++e) v[e] = s[min(j0 + e * CH_NT + tid, c1 - 1)];
+  };
+  load(c0);                                                      // in flight during find_digit
   uint32_t* w = ws_list(a, list);
   uint32_t b1, rem1;
   find_digit<CH_NT, 2048>(w + W_HIST1, (uint32_t)li.kk, sh, b1, rem1);
-  for (int i = threadIdx.x; i < 2048; i += CH_NT) hist2[i] = 0u;
+  for (int i = tid; i < 2048; i += CH_NT) hist2[i] = 0u;
   __syncthreads();
-  const float* s = a.scores + (size_t)list * a.s_stride;
   uint2* cand = (uint2*)(w + a.cand_off);
-  const int lane = threadIdx.x & 63;
   uint32_t gt = 0;
-  for (int j0 = c0; j0 < c1; j0 += CH_NT) {                      // uniform trip count for the ballot
-    const int j = j0 + threadIdx.x;
-    uint32_t key = 0u;
-    bool in = false;
-    if (j < c1) {
-      key = f32_key(s[j]);
-      const uint32_t d1 = key >> 21;
-      gt += d1 > b1 ? 1u : 0u;
-      in = d1 == b1;
+  for (int j0 = c0; j0 < c1; j0 += PER * CH_NT) {
+    if (j0 != c0) load(j0);
+    uint32_t key[PER], in = 0u;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      key[e] = f32_key(v[e]);
+      const bool ok = j0 + e * CH_NT + tid < c1;
+      const uint32_t d1 = key[e] >> 21;
+      gt += (ok && d1 > b1) ? 1u : 0u;
+      in |= (ok && d1 == b1 ? 1u : 0u) << e;
     }
-    const uint64_t m = __ballot(in);
-    if (m) {
-      uint32_t base = 0;
-      if (lane == 0) base = atomicAdd(&w[W_CCOUNT], (uint32_t)__popcll(m));
-      base = __shfl(base, 0);
-      if (in) {
-        const uint32_t slot = base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
-        cand[slot] = make_uint2(key, (uint32_t)j);
-        atomicAdd(&hist2[(key >> 10) & 0x7FFu], 1u);
+    // one reservation in the list's candidate buffer per workgroup and batch
+    uint32_t tot;
+    uint32_t slot = block_scan_excl<CH_NT>((uint32_t)__builtin_popcount(in), sh, tot, false);
+    if (tot == 0u) continue;                                     // uniform over the block
+    if (tid == 0) s_base = atomicAdd(&w[W_CCOUNT], tot);
+    __syncthreads();
+    slot += s_base;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < PER; ++e)
+      if ((in >> e) & 1u) {
+        cand[slot++] = make_uint2(key[e], (uint32_t)(j0 + e * CH_NT + tid));
+        atomicAdd(&hist2[(key[e] >> 10) & 0x7FFu], 1u);
       }
-    }
   }
   uint32_t tot;
   block_scan_excl<CH_NT>(gt, sh, tot, false);
-  if (threadIdx.x == 0) w[W_CHUNKS + blockIdx.x] = tot;           // keys above the boundary bin
+  if (tid == 0) w[W_CHUNKS + blockIdx.x] = tot;                  // keys above the boundary bin
   __syncthreads();
-  for (int i = threadIdx.x; i < 2048; i += CH_NT)
+  for (int i = tid; i < 2048; i += CH_NT)
     if (hist2[i]) atomicAdd(&w[W_HIST2 + i], hist2[i]);
 }
 
@@ -201,6 +213,15 @@ __global__ __launch_bounds__(FIN_NT) void sel_finalize_kernel(SelectArgs a) {
   __shared__ uint32_t hist3[1024];
   __shared__ uint32_t gtx[1024], eqc[1024];
   uint32_t* w = ws_list(a, list);
+  const uint32_t nc = w[W_CCOUNT];
+  const uint2* cand = (const uint2*)(w + a.cand_off);
+  constexpr int CPT = 4;                                          // candidates per thread per batch
+  uint2 cr[CPT];
+  auto cload = [&](uint32_t i0) {                                 // clamped: in bounds, no branch
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) cr[u] = cand[min(i0 + u * FIN_NT + tid, max(nc, 1u) - 1u)];
+  };
+  cload(0);                                                       // in flight during the first two digits
   uint32_t b1, rem1, b2, rem2, b3, rem3;
   find_digit<FIN_NT, 2048>(w + W_HIST1, (uint32_t)li.kk, sh, b1, rem1);
   find_digit<FIN_NT, 2048>(w + W_HIST2, rem1, sh, b2, rem2);
@@ -208,21 +229,25 @@ __global__ __launch_bounds__(FIN_NT) void sel_finalize_kernel(SelectArgs a) {
   gtx[tid] = 0u;
   eqc[tid] = 0u;
   __syncthreads();
-  const uint32_t nc = w[W_CCOUNT];
-  const uint2* cand = (const uint2*)(w + a.cand_off);
-  for (uint32_t i = tid; i < nc; i += FIN_NT) {
-    const uint32_t key = cand[i].x;
-    if (((key >> 10) & 0x7FFu) == b2) atomicAdd(&hist3[key & 0x3FFu], 1u);
+  for (uint32_t i0 = 0; i0 < nc; i0 += CPT * FIN_NT) {
+    if (i0) cload(i0);
+#pragma unroll
+    for (int u = 0; u < CPT; ++u)
+      if (i0 + u * FIN_NT + tid < nc && ((cr[u].x >> 10) & 0x7FFu) == b2) atomicAdd(&hist3[cr[u].x & 0x3FFu], 1u);
   }
   __syncthreads();
   find_digit<FIN_NT, 1024>(hist3, rem2, sh, b3, rem3);
   const uint32_t T = (b1 << 21) | (b2 << 10) | b3;
   const uint32_t need = rem3;                                     // keys == T taken, lowest index first
-  for (uint32_t i = tid; i < nc; i += FIN_NT) {
-    const uint2 c = cand[i];
-    const int ch = (int)(c.y / (uint32_t)a.chunk);
-    if (c.x > T) atomicAdd(&gtx[ch], 1u);
-    else if (c.x == T) atomicAdd(&eqc[ch], 1u);
+  for (uint32_t i0 = 0; i0 < nc; i0 += CPT * FIN_NT) {
+    if (nc > CPT * FIN_NT) cload(i0);                             // else the registers hold them all
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      if (i0 + u * FIN_NT + tid >= nc) continue;
+      const int ch = (int)(cr[u].y / (uint32_t)a.chunk);
+      if (cr[u].x > T) atomicAdd(&gtx[ch], 1u);
+      else if (cr[u].x == T) atomicAdd(&eqc[ch], 1u);
+    }
   }
   __syncthreads();
   // per-chunk prefix: ties before the chunk, then the output offset of the chunk
@@ -256,6 +281,13 @@ __global__ __launch_bounds__(CH_NT) void sel_write_kernel(SelectArgs a) {
     for (int j = c0 + threadIdx.x; j < c1; j += CH_NT) out[j] = j;
     return;
   }
+  const float* s = a.scores + (size_t)list * a.s_stride;
+  float v[E];
+  auto load = [&](int p0) {                                      // coalesced, clamped, all in flight
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = s[min(p0 + e * CH_NT + (int)threadIdx.x, c1 - 1)];
+  };
+  load(c0);                                                      // before the workspace reads
   const uint32_t* w = ws_list(a, list);
   const int ch = blockIdx.x;
   const uint32_t nsel = w[W_CHUNKS + 3 * a.max_chunks + ch];
@@ -265,10 +297,14 @@ __global__ __launch_bounds__(CH_NT) void sel_write_kernel(SelectArgs a) {
   uint32_t ties = w[W_CHUNKS + 2 * a.max_chunks + ch];
   __shared__ float stage[E * CH_NT];
   __shared__ uint32_t sh[3 * (CH_NT / 64) + 3];
-  const float* s = a.scores + (size_t)list * a.s_stride;
   for (int p0 = c0; p0 < c1; p0 += E * CH_NT) {
     const int pn = min(E * CH_NT, c1 - p0);
-    for (int i = threadIdx.x; i < pn; i += CH_NT) stage[i] = s[p0 + i];
+    if (p0 != c0) {
+      __syncthreads();                                           // previous batch read from stage
+      load(p0);
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) stage[e * CH_NT + threadIdx.x] = v[e];
     __syncthreads();
     uint32_t gt = 0u, eq = 0u;
 #pragma unroll

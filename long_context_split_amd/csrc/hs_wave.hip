@@ -67,15 +67,62 @@ __global__ __launch_bounds__(64 * NW) void attn_wave_kernel(AttnArgs a) {
   int b, t0, g;
   if (GATHER) { g = list % a.n_kv; const int bt = list / a.n_kv; b = bt / a.n_q; t0 = bt % a.n_q; }
   else { g = list % a.n_kv; b = list / a.n_kv; t0 = 0; }
+  const int c0 = chunk * a.chunk;
+  // GATHER: the rows of this wave's first tile come straight from the index list (clamped into the
+  // list, validated below), issued before anything else so the K/V loads wait for one load only.
+  const int32_t* il = GATHER ? a.sel_idx + (size_t)list * a.sel_cap : nullptr;
+  const int cend = GATHER ? min(c0 + a.chunk, a.sel_cap) : 0;
+  int frow[GATHER ? PPL : 1], fsrow = 0;
+  if (GATHER) {
+#pragma unroll
+    for (int i = 0; i < PPL; ++i) frow[i] = il[min(c0 + wave * 32 + (lane + 64 * i) / PPR, cend - 1)];
+    if (FP8) fsrow = il[min(c0 + wave * 32 + (lane & 31), cend - 1)];
+  }
   const int Lb = a.seq_len[b];
   const int ntok = GATHER ? min(max(a.sel_count[(size_t)list], 0), a.sel_cap) : Lb;
-  const int c0 = chunk * a.chunk;
   if (c0 >= ntok) return;
   const int c1 = min(ntok, c0 + a.chunk);
   const int64_t rs = a.row_start[b];
   const char* kbase = (const char*)a.k + ((size_t)rs * a.n_kv + g) * SB;
   const char* vbase = (const char*)a.v + ((size_t)rs * a.n_kv + g) * SB;
   const size_t rstride = (size_t)a.n_kv * SB;
+  const int ntiles = (c1 - c0 + 31) / 32;
+
+  char* const kt = smem + wave * 2 * 32 * ROWB;
+  char* const vt = kt + 32 * ROWB;
+  float* const wks = FP8 ? ksc + wave * 32 : nullptr;
+  float* const wvs = FP8 ? vsc + wave * 32 : nullptr;
+
+  // Cache row of a tile position, clamped into the list so every load stays in bounds and needs no
+  // branch (a branch around a load makes the compiler wait for it at the join); positions past the
+  // chunk and invalid indices are masked in the softmax instead.
+  auto tok_row = [&](int tile, int tok) -> int {
+    const int pos = min(c0 + tile * 32 + tok, c1 - 1);
+    return GATHER ? max(gidx[pos - c0], 0) : pos;
+  };
+  auto valid_row = [&](int j) -> int { return (j >= 0 && j < Lb) ? j : 0; };
+  u32x4 rk[PPL], rv[PPL];
+  float sk = 0.f, sv = 0.f;
+  auto load_rows = [&](auto row_of, int srow) {
+#pragma unroll
+    for (int i = 0; i < PPL; ++i) {
+      const size_t off = (size_t)row_of(i) * rstride + ((lane + 64 * i) % PPR) * 16;
+      rk[i] = *(const u32x4*)(kbase + off);
+      rv[i] = *(const u32x4*)(vbase + off);
+    }
+    if (FP8) {
+      sk = a.k_scale[((size_t)rs + srow) * a.n_kv + g];
+      sv = a.v_scale[((size_t)rs + srow) * a.n_kv + g];
+    }
+  };
+  auto load = [&](int tile) {
+    load_rows([&](int i) { return tok_row(tile, (lane + 64 * i) / PPR); }, FP8 ? tok_row(tile, lane & 31) : 0);
+  };
+  if (wave < ntiles) {                                            // first tile, before the Q barrier
+    if (GATHER) load_rows([&](int i) { return valid_row(frow[i]); }, valid_row(fsrow));
+    else load_rows([&](int i) { return min(c0 + wave * 32 + (lane + 64 * i) / PPR, c1 - 1); },
+                   min(c0 + wave * 32 + (lane & 31), c1 - 1));
+  }
 
   // Q rows -> LDS (row r = tt*G + hh; rows >= R are zero)
   for (int p = tid; p < 32 * 16; p += NT) {
@@ -94,7 +141,6 @@ __global__ __launch_bounds__(64 * NW) void attn_wave_kernel(AttnArgs a) {
     *(u32x4*)(qs + r * ROWB + c * 16) = x;
   }
   if (GATHER) {
-    const int32_t* il = a.sel_idx + (size_t)list * a.sel_cap;
     for (int i = tid; i < c1 - c0; i += NT) {
       const int j = il[c0 + i];
       gidx[i] = (j >= 0 && j < Lb) ? j : -1;
@@ -102,35 +148,6 @@ __global__ __launch_bounds__(64 * NW) void attn_wave_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  char* const kt = smem + wave * 2 * 32 * ROWB;
-  char* const vt = kt + 32 * ROWB;
-  float* const wks = FP8 ? ksc + wave * 32 : nullptr;
-  float* const wvs = FP8 ? vsc + wave * 32 : nullptr;
-  const int ntiles = (c1 - c0 + 31) / 32;
-
-  // Cache row of a tile position, clamped into the list so every load stays in bounds and needs no
-  // branch (a branch around a load makes the compiler wait for it at the join); positions past the
-  // chunk and invalid indices are masked in the softmax instead.
-  auto tok_row = [&](int tile, int tok) -> int {
-    const int pos = min(c0 + tile * 32 + tok, c1 - 1);
-    return GATHER ? max(gidx[pos - c0], 0) : pos;
-  };
-  u32x4 rk[PPL], rv[PPL];
-  float sk = 0.f, sv = 0.f;
-  auto load = [&](int tile) {
-#pragma unroll
-    for (int i = 0; i < PPL; ++i) {
-      const int p = lane + 64 * i, tok = p / PPR, c = p % PPR;
-      const size_t off = (size_t)tok_row(tile, tok) * rstride + c * 16;
-      rk[i] = *(const u32x4*)(kbase + off);
-      rv[i] = *(const u32x4*)(vbase + off);
-    }
-    if (FP8) {
-      const size_t r = (size_t)rs + tok_row(tile, lane & 31);
-      sk = a.k_scale[r * a.n_kv + g];
-      sv = a.v_scale[r * a.n_kv + g];
-    }
-  };
   auto store = [&]() {
 #pragma unroll
     for (int i = 0; i < PPL; ++i) {
@@ -163,7 +180,6 @@ __global__ __launch_bounds__(64 * NW) void attn_wave_kernel(AttnArgs a) {
   float m = -INFINITY, lsum = 0.f;
   f32x16 acc[4] = {};
   const float sl2 = a.scale_log2;
-  if (wave < ntiles) load(wave);
   for (int tile = wave; tile < ntiles; tile += NW) {
     wave_sync();
     store();
@@ -355,9 +371,12 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
   const size_t rstride = (size_t)a.n_kv * SB;
   const int ntiles = (c1 - c0 + TT - 1) / TT;
   char* const kt = ktile[wave];
-  u32x4 kr[PPL];
-  float ks = 0.f;
-  auto load = [&](int tile) {                                    // clamped rows: no branch, in bounds
+  // Two tiles in flight per wave: buffers A and B alternate (named, so every wait is a static count).
+  // Loads are clamped to the wave's last tile instead of skipped, so no branch surrounds a load; the
+  // repeated tile at the end hits in cache.
+  u32x4 kA[PPL], kB[PPL];
+  float sA = 0.f, sB = 0.f;
+  auto load = [&](u32x4 (&kr)[PPL], float& ks, int tile) {      // clamped rows: no branch, in bounds
 #pragma unroll
     for (int i = 0; i < PPL; ++i) {
       const int p = lane + 64 * i;
@@ -368,8 +387,7 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
   };
   const int tpw = a.G >= 32 ? 1 : 32 / a.G;                      // query tokens in the 32 rows
   float* sout = a.scores + (size_t)b * a.n_q * a.n_kv * a.s_stride;
-  if (wave < ntiles) load(wave);
-  for (int tile = wave; tile < ntiles; tile += NW) {
+  auto process = [&](const u32x4 (&kr)[PPL], float ks, int tile) {
     wave_sync();
 #pragma unroll
     for (int i = 0; i < PPL; ++i) {                              // registers -> LDS (FP8 -> bf16)
@@ -393,7 +411,6 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
     }
     if (FP8) ksc[wave][lane] = ks;
     wave_sync();
-    if (tile + NW < ntiles) load(tile + NW);                     // in flight during the two sub-tiles
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       f32x16 s = {};
@@ -433,6 +450,18 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
           if (do_hist) atomicAdd(&hist[t][f32_key(tv[t]) >> 21], 1u);
         }
       }
+    }
+  };
+  if (wave < ntiles) {
+    const int last = wave + NW * ((ntiles - 1 - wave) / NW);     // this wave's last tile
+    load(kA, sA, wave);
+    load(kB, sB, min(wave + NW, last));
+    for (int tile = wave; tile < ntiles; tile += 2 * NW) {
+      process(kA, sA, tile);
+      load(kA, sA, min(tile + 2 * NW, last));
+      if (tile + NW >= ntiles) break;
+      process(kB, sB, tile + NW);
+      load(kB, sB, min(tile + 3 * NW, last));
     }
   }
   if (!do_hist) return;

@@ -83,3 +83,16 @@ def test_select_one_million_candidates():
     x = (rng.random(n) * 1e-4).astype(np.float32)
     x[rng.choice(n, 1500, replace=False)] = np.float32(3e-4)        # ties at the boundary
     _check(x.reshape(1, 1, 1, n), [L], 1, 1, 1024, 128)
+
+
+def test_select_more_than_four_million_candidates():
+    """Over 4M candidates the per-chunk kernels take several batches per workgroup; the
+    second list puts every score into one first-digit bin (millions of candidates)."""
+    banner("select L=5000128, two lists")
+    rng = np.random.default_rng(11)
+    L = 5_000_128
+    n = L - 128
+    x = np.empty((2, 1, 1, n), np.float32)
+    x[0, 0, 0] = rng.random(n, dtype=np.float32)
+    x[1, 0, 0] = (1.0 + rng.random(n) * 0.01).astype(np.float32)
+    _check(x, [L, L], 1, 1, 1024, 128)
