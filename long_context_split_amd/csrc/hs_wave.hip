@@ -291,7 +291,7 @@ __global__ __launch_bounds__(64 * NW) void attn_wave_kernel(AttnArgs a) {
 }
 
 // Score pass: each wave streams 64-token K tiles (coalesced 1 KB loads) with
-// one tile prefetched in registers while the previous one, staged in the
+// two tiles in flight in registers while the current one, staged in the
 // wave's own LDS slice, feeds the MFMA B operand (S = Q K^T: lane = token, 16
 // rows per lane), so the sum over a query token's heads is mostly in-lane.
 template <int KVT, int NW, int NQ>
@@ -316,6 +316,31 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
   const int w = min(a.window, Lb);
   const int ncand = Lb - w;
   const int c0 = blockIdx.x * a.chunk;
+  const int c1 = min(ncand, c0 + a.chunk);
+  const int64_t rs = a.row_start[b];
+  const char* kbase = (const char*)a.k + ((size_t)rs * a.n_kv + g) * SB;
+  const size_t rstride = (size_t)a.n_kv * SB;
+  const int ntiles = c1 > c0 ? (c1 - c0 + TT - 1) / TT : 0;
+  char* const kt = ktile[wave];
+  // Two tiles in flight per wave: buffers A and B alternate (named, so every wait is a static count).
+  // Loads are clamped to the wave's last tile instead of skipped, so no branch surrounds a load; the
+  // repeated tile at the end hits in cache.
+  u32x4 kA[PPL], kB[PPL];
+  float sA = 0.f, sB = 0.f;
+  auto load = [&](u32x4 (&kr)[PPL], float& ks, int tile) {      // clamped rows: no branch, in bounds
+#pragma unroll
+    for (int i = 0; i < PPL; ++i) {
+      const int p = lane + 64 * i;
+      const int pos = min(c0 + tile * TT + p / PPR, c1 - 1);
+      kr[i] = *(const u32x4*)(kbase + (size_t)pos * rstride + (p % PPR) * 16);
+    }
+    if (FP8) ks = a.k_scale[((size_t)rs + min(c0 + tile * TT + lane, c1 - 1)) * a.n_kv + g];
+  };
+  const int last = wave + NW * (max(ntiles - 1 - wave, 0) / NW);  // this wave's last tile
+  if (wave < ntiles) {                                           // in flight during the prologue below
+    load(kA, sA, wave);
+    load(kB, sB, min(wave + NW, last));
+  }
   if (a.part_ml) {
     // The full layer's merge, folded in (at most 64 chunks): every workgroup derives the LSE of all rows
     // from the chunk partials; row r's output is merged by workgroup r % nwg of the list's nwg >= 1.
@@ -337,7 +362,6 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
     }
   }
   if (c0 >= ncand) return;
-  const int c1 = min(ncand, c0 + a.chunk);
   const bool do_hist = a.hist != nullptr;
   if (do_hist)
     for (int i = tid; i < NQ * 2048; i += NT) hist[i >> 11][i & 2047] = 0u;
@@ -366,25 +390,6 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
     const float v = a.part_ml ? s_lse2[rc] : a.lse2[((size_t)b * a.n_q + rc / a.G) * a.H + (size_t)g * a.G + rc % a.G];
     lse2[r] = rw < a.R ? v : INFINITY;
   }
-  const int64_t rs = a.row_start[b];
-  const char* kbase = (const char*)a.k + ((size_t)rs * a.n_kv + g) * SB;
-  const size_t rstride = (size_t)a.n_kv * SB;
-  const int ntiles = (c1 - c0 + TT - 1) / TT;
-  char* const kt = ktile[wave];
-  // Two tiles in flight per wave: buffers A and B alternate (named, so every wait is a static count).
-  // Loads are clamped to the wave's last tile instead of skipped, so no branch surrounds a load; the
-  // repeated tile at the end hits in cache.
-  u32x4 kA[PPL], kB[PPL];
-  float sA = 0.f, sB = 0.f;
-  auto load = [&](u32x4 (&kr)[PPL], float& ks, int tile) {      // clamped rows: no branch, in bounds
-#pragma unroll
-    for (int i = 0; i < PPL; ++i) {
-      const int p = lane + 64 * i;
-      const int pos = min(c0 + tile * TT + p / PPR, c1 - 1);
-      kr[i] = *(const u32x4*)(kbase + (size_t)pos * rstride + (p % PPR) * 16);
-    }
-    if (FP8) ks = a.k_scale[((size_t)rs + min(c0 + tile * TT + lane, c1 - 1)) * a.n_kv + g];
-  };
   const int tpw = a.G >= 32 ? 1 : 32 / a.G;                      // query tokens in the 32 rows
   float* sout = a.scores + (size_t)b * a.n_q * a.n_kv * a.s_stride;
   auto process = [&](const u32x4 (&kr)[PPL], float ks, int tile) {
@@ -453,9 +458,6 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
     }
   };
   if (wave < ntiles) {
-    const int last = wave + NW * ((ntiles - 1 - wave) / NW);     // this wave's last tile
-    load(kA, sA, wave);
-    load(kB, sB, min(wave + NW, last));
     for (int tile = wave; tile < ntiles; tile += 2 * NW) {
       process(kA, sA, tile);
       load(kA, sA, min(tile + 2 * NW, last));
