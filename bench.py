@@ -41,6 +41,7 @@ def kernel_digest():
         h.update(open(os.path.join(ROOT, f), "rb").read())
     return h.hexdigest()[:16]
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def log(msg):
@@ -52,8 +53,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 5],
-                    help="2: 32 x 128K bf16 (default); 5: ragged 8 x 64K-512K, 4 blocks")
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 5],
+                    help="2: 32 x 128K bf16 (default); 3: 1 x 1M FP8 E4M3, 64 heads, 4 query tokens; "
+                         "5: ragged 8 x 64K-512K, 4 blocks")
     ap.add_argument("--L", type=int, default=None, help="context length override (sweeps)")
     ap.add_argument("--B", type=int, default=None, help="batch override (sweeps)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle time budget")
@@ -93,9 +95,12 @@ def main():
     blocks = []
     for blk in range(n_blocks):
         case = synth.decode_case(args.config, L=args.L, B=args.B, block=blk)
-        k = torch.from_numpy(case["k"].view(np.int16)).to(dev).view(torch.bfloat16)
-        v = torch.from_numpy(case["v"].view(np.int16)).to(dev).view(torch.bfloat16)
-        kv = hs.KVCache(k, v, case["lengths"], case["row_start"])
+        if spec["kv"] == "bf16":
+            k = torch.from_numpy(case["k"].view(np.int16)).to(dev).view(torch.bfloat16)
+            v = torch.from_numpy(case["v"].view(np.int16)).to(dev).view(torch.bfloat16)
+            kv = hs.KVCache(k, v, case["lengths"], case["row_start"])
+        else:
+            kv = fp8_cache(case, dev)
         qf = torch.from_numpy(case["q_full"].view(np.int16)).to(dev).view(torch.bfloat16)
         qs = [torch.from_numpy(q.view(np.int16)).to(dev).view(torch.bfloat16) for q in case["q_sparse"]]
         blocks.append(dict(case=case, kv=kv, qf=qf, qs=qs))
@@ -198,7 +203,8 @@ def main():
             f"per step {d['total_ms_per_step'] * 1e3:9.2f} us")
 
     # ---------------------------------------------------------------- algorithmic bytes
-    row_bytes = 2 * 128 * 2                                     # bf16 K + V row
+    fp8 = spec["kv"] == "e4m3"
+    row_bytes = 2 * 128 + 8 if fp8 else 2 * 128 * 2             # K + V row (+ two fp32 scales for E4M3)
     sum_L = int(sum(int(x) for x in lens))
     union_rows = 0
     for bl in blocks:
@@ -216,15 +222,26 @@ def main():
     k1_name = "attn_wave_dense" if "attn_wave_dense" in kern else "attn_partial_dense"
     k1 = kern.get(k1_name)
     k1_bytes = sum_L * row_bytes                                 # per launch (one block's full layer)
+    # dense MFMA work of the pass: S = Q K^T and O = P V over every row, 2 * 2 * rows * L * d
+    k1_flops = 4.0 * n_q * H * 128 * sum_L
     roof = None
     if k1:
-        ach = k1_bytes / (k1["avg_ms"] * 1e-3) / 1e9
+        sec = k1["avg_ms"] * 1e-3
         default_workload = args.config == 2 and args.L is None and args.B is None
         traffic = KNOWN_TRAFFIC.get(kernel_digest()) if default_workload else None
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": k1_name,
-                "algorithmic_bytes_per_launch": k1_bytes, "avg_launch_us": round(k1["avg_ms"] * 1e3, 2),
-                "dominant_kernel_by_time": dom}
+        t_hbm, t_mfma = k1_bytes / (HBM_PEAK_GBPS * 1e9), k1_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+        if t_hbm >= t_mfma:
+            ach = k1_bytes / sec / 1e9
+            roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBPS, 4)}
+        else:
+            ach = k1_flops / sec / 1e12
+            roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "hbm_GBps": round(k1_bytes / sec / 1e9, 1)}
+        roof.update({"traffic": traffic, "kernel": k1_name, "algorithmic_bytes_per_launch": k1_bytes,
+                     "algorithmic_flops_per_launch": k1_flops, "avg_launch_us": round(k1["avg_ms"] * 1e3, 2),
+                     "dominant_kernel_by_time": dom})
 
     # ---------------------------------------------------------------- KV Bridging (prefill side)
     bridge = None if args.no_bridge else bench_bridge(dev, args.bridge_iters)
@@ -239,7 +256,7 @@ def main():
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(blocks[0]["case"], top_k, window, args.cpu_seconds)
+        cpu = cpu_baseline(blocks[0]["case"], spec, top_k, window, args.cpu_seconds)
 
     line = {
         "metric": METRIC,
@@ -259,7 +276,7 @@ def main():
             f"{spec['name']}_L{args.L or 'cfg'}_B{args.B or 'cfg'}",
             "batch": B, "seq_len": int(lens.max()) if args.config == 2 else [int(x) for x in lens],
             "query_heads": H, "kv_heads": 1, "head_dim": 128, "q_tokens": n_q, "top_k": top_k, "window": window,
-            "sparse_layers": n_sparse, "blocks": n_blocks, "kv_dtype": "bf16",
+            "sparse_layers": n_sparse, "blocks": n_blocks, "kv_dtype": spec["kv"],
         },
         "achieved_hbm_GBps": round(eff_gbps, 1),
         "hbm_frac": round(eff_gbps / HBM_PEAK_GBPS, 4),
@@ -276,6 +293,29 @@ def main():
                   "; kernel durations from per-launch HIP events on the library stream in a second (eager) region",
     }
     print(json.dumps(line), flush=True)
+
+
+def fp8_cache(case, dev):
+    """An E4M3 cache (codes + per-row scales) of the case's float32 K and V rows, quantised on the GPU
+    by the library's own KV Bridging with identity projections (K = X I exactly, then the per-row
+    E4M3 quantiser); X is the bf16 rounding of the float32 rows."""
+    import numpy as np
+    import torch
+    from long_context_split_amd import hysparse as hs
+    n = case["k"].shape[0]
+    eye = torch.eye(128, dtype=torch.bfloat16, device=dev)
+    codes = [torch.empty((n, 1, 128), dtype=torch.uint8, device=dev) for _ in range(3)]
+    scales = [torch.empty((n, 1), dtype=torch.float32, device=dev) for _ in range(3)]
+    # target 0 receives K's codes (and a discarded copy as V); target 1 receives V's codes
+    t_k = hs.KVCache(codes[0], codes[2], None, None, scales[0], scales[2])
+    t_v = hs.KVCache(codes[2], codes[1], None, None, scales[2], scales[1])
+    for src, tgt in ((case["k"], t_k), (case["v"], t_v)):
+        x = torch.from_numpy(np.ascontiguousarray(src.reshape(n, 128))).to(dev).to(torch.bfloat16)
+        hs.kv_bridge(x, [eye], [eye], [tgt], 0)
+        torch.cuda.synchronize()
+        del x
+    del codes[2], scales[2]
+    return hs.KVCache(codes[0], codes[1], case["lengths"], case["row_start"], scales[0], scales[1])
 
 
 def bench_bridge(dev, iters):
@@ -316,10 +356,10 @@ def bench_bridge(dev, iters):
             "frac": round(tflops / 2500.0, 4), "flops": flops, "bytes": in_bytes + out_bytes}
 
 
-def cpu_baseline(case, top_k, window, budget_s):
+def cpu_baseline(case, spec, top_k, window, budget_s):
     """The float64 oracle, as it stands, on sequences of the same workload until the budget is spent."""
     import numpy as np
-    from oracle import attention, block
+    from oracle import attention, block, bridge as obridge
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -331,8 +371,14 @@ def cpu_baseline(case, top_k, window, budget_s):
     done = 0
     for i in range(len(lens)):
         L, r0 = int(lens[i]), int(starts[i])
-        k = block.cache_values(case["k"][r0:r0 + L], "bf16")
-        v = block.cache_values(case["v"][r0:r0 + L], "bf16")
+        if spec["kv"] == "bf16":
+            k = block.cache_values(case["k"][r0:r0 + L], "bf16")
+            v = block.cache_values(case["v"][r0:r0 + L], "bf16")
+        else:                                   # the oracle's own E4M3 quantiser, then its decoder
+            kc, ksc = obridge.quantize_rows_e4m3(case["k"][r0:r0 + L].reshape(L, 128))
+            vc, vsc = obridge.quantize_rows_e4m3(case["v"][r0:r0 + L].reshape(L, 128))
+            k = block.cache_values(kc.reshape(L, 1, 128), "e4m3", ksc.reshape(L, 1))
+            v = block.cache_values(vc.reshape(L, 1, 128), "e4m3", vsc.reshape(L, 1))
         q = block.cache_values(case["q_full"][i], "bf16")
         out = block.full_layer(q, k, v, top_k, window)
         for qs in case["q_sparse"]:

@@ -146,6 +146,8 @@ int kv_type(hs_dtype d) { return d == HS_F32 ? hs::KV_F32 : d == HS_BF16 ? hs::K
 
 struct FullPlan {
   int wave;  // 1: at most 32 query rows per KV head on a bf16 / FP8 cache -> attn_wave kernel
+  int rows;  // 1: more rows, bf16 / FP8 cache -> attn_rows kernel (nrg row groups per workgroup)
+  int nrg;
   int ct, nwr, G, R, n_lists, chunk, max_chunks;
   int nwr_s, chunk_s, max_chunks_s;
   int64_t s_stride;
@@ -169,14 +171,20 @@ hs_status plan_full(const hs_kv_cache* kv, const hs_attn_params* p, hs_dtype q_d
   pl.nwr = pl.ct == hs::CT_F32 ? (pl.R <= 32 ? 1 : 4) : hs::rows_per_wave_group(pl.R);
   pl.n_lists = ci.B * ci.n_kv;
   pl.wave = pl.ct == hs::CT_BF16 && pl.R <= 32;
-  const int tt = pl.wave ? 256 : hs::partial_tile_tokens(pl.nwr);
-  const int zb = (pl.R + 32 * pl.nwr - 1) / (32 * pl.nwr);
+  pl.rows = pl.ct == hs::CT_BF16 && pl.R > 32;
+  pl.nrg = pl.rows ? hs::rows_groups(pl.R) : 0;
+  const int tt = pl.wave ? 256 : pl.rows ? hs::rows_tile_tokens(pl.nrg) : hs::partial_tile_tokens(pl.nwr);
+  const int zb = pl.rows ? (pl.R + 32 * pl.nrg - 1) / (32 * pl.nrg) : (pl.R + 32 * pl.nwr - 1) / (32 * pl.nwr);
   int chunk = env_int("HS_SPLIT_TOKENS", 0);
   if (chunk <= 0) {
     if (pl.wave) {
       // about 512 workgroups (2 per CU-slot round), 1024..32768 tokens each
       const int64_t per = (ci.total + 511) / 512;
       chunk = (int)std::min<int64_t>(32768, std::max<int64_t>(1024, per));
+    } else if (pl.rows) {
+      // about 256 workgroups (one per CU: compute-bound, and few partials to merge), >= one super-tile
+      const int64_t per = (ci.total * zb + 255) / 256;
+      chunk = (int)std::min<int64_t>(32768, std::max<int64_t>(tt, per));
     } else {
       // about 1024 work items over the whole batch, 512..16384 tokens each
       const int64_t per = (ci.total * zb + 1023) / 1024;
@@ -344,7 +352,12 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
   a.part_acc = (float*)(ws + pl.off_acc); a.part_ml = (float*)(ws + pl.off_ml);
   a.direct = pl.wave && pl.max_chunks == 1; a.out = out; a.lse = lse; a.lse2 = lse2;
   const int n_sel_lists = ci.B * p->q_tokens * ci.n_kv;
-  if (pl.wave) {
+  // the many-row score kernel builds the selection's first-digit histogram when a workgroup spans
+  // at most 4 query tokens
+  const bool rows_scores = pl.rows && pl.G >= 16;
+  const bool rows_hist = rows_scores && (pl.G >= 32 * pl.nrg ? 1 : 32 * pl.nrg / pl.G) <= 4;
+  const bool fused_prefix = pl.wave || rows_hist;
+  if (fused_prefix) {
     a.zero_ptr = (uint32_t*)(ws + pl.off_sel);                 // the selection's histograms, cleared here
     a.zero_stride = pl.sel.ws_stride;
     a.zero_words = hs::SELECT_ZERO_WORDS;
@@ -353,6 +366,8 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
   hipError_t e;
   if (pl.wave)
     e = timed("attn_wave_dense", s, [&] { return hs::launch_attn_wave(a, kvt, false, s); });
+  else if (pl.rows)
+    e = timed("attn_rows_dense", s, [&] { return hs::launch_attn_rows(a, kvt, pl.nrg, s); });
   else
     e = timed("attn_partial_dense", s, [&] { return hs::launch_attn_partial(a, kvt, pl.ct, pl.nwr, false, s); });
   if (e != hipSuccess) return hip_fail(e, "full attention pass 1");
@@ -372,7 +387,15 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
     sa.q = q; sa.q_f32 = a.q_f32; sa.n_kv = ci.n_kv; sa.H = a.H; sa.G = pl.G; sa.n_q = a.n_q; sa.R = pl.R;
     sa.n_lists = pl.n_lists; sa.window = p->window; sa.chunk = pl.chunk_s; sa.max_chunks = pl.max_chunks_s;
     sa.scale_log2 = sl2; sa.lse2 = lse2; sa.scores = scores; sa.s_stride = pl.s_stride;
-    if (pl.wave) {
+    if (rows_scores) {
+      if (rows_hist) {
+        sa.hist = (uint32_t*)(ws + pl.off_sel);
+        sa.hist_stride = pl.sel.ws_stride;
+      }
+      if ((e = timed("attn_rows_scores", s, [&] { return hs::launch_attn_rows_scores(sa, kvt, pl.nrg, s); })) !=
+          hipSuccess)
+        return hip_fail(e, "selection scores");
+    } else if (pl.wave) {
       sa.hist = (uint32_t*)(ws + pl.off_sel);
       sa.hist_stride = pl.sel.ws_stride;
       if (fold_merge) {
@@ -393,7 +416,7 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
   se.sel_idx = sel_idx; se.sel_count = sel_count;
   se.ws = (uint32_t*)(ws + pl.off_sel); se.ws_stride = pl.sel.ws_stride; se.cand_off = pl.sel.cand_off;
   se.chunk = pl.sel.chunk; se.max_chunks = pl.sel.max_chunks;
-  if ((e = timed("select_topk", s, [&] { return hs::launch_select(se, n_sel_lists, pl.wave, s); })) != hipSuccess)
+  if ((e = timed("select_topk", s, [&] { return hs::launch_select(se, n_sel_lists, fused_prefix, s); })) != hipSuccess)
     return hip_fail(e, "selection");
   return HS_OK;
 }

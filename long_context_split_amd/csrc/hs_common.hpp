@@ -15,6 +15,7 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
@@ -32,6 +33,21 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   uint32_t em = c & 0x7Fu;
   float v = (em >= 8u) ? __uint_as_float((em + (120u << 3)) << 20) : (float)em * 0x1p-9f;
   return __uint_as_float(__float_as_uint(v) | ((c & 0x80u) << 24));
+}
+
+// Two floats -> two bf16 (round to nearest even; the conversion instruction, checked bit for bit
+// against the rounding on the bits, ties and subnormals included) packed low-first in a word.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2 r = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Four OCP E4M3FN codes (bytes of w, low first) -> four bf16 packed in two words (lo: bytes 0, 1;
+// hi: bytes 2, 3), exact: every finite E4M3 value is a bf16 value.  gfx950's conversion instruction
+// with unit scale (checked against the format definition on every non-NaN code).
+__device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
 }
 
 // float32 -> OCP E4M3FN code: round to nearest, ties to the even mantissa,
@@ -67,6 +83,17 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
   return v;
+}
+
+// Clears runs of words with the whole grid (any grid shape): `lists` runs of `words` words,
+// `stride` words apart.  No-op when ptr is null.
+__device__ __forceinline__ void zero_words_grid(uint32_t* ptr, int64_t stride, int words, int lists) {
+  if (!ptr) return;
+  const int64_t total = (int64_t)lists * words;
+  const int64_t nwg = (int64_t)gridDim.x * gridDim.y * gridDim.z;
+  const int64_t wg = ((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+  for (int64_t i = wg * blockDim.x + threadIdx.x; i < total; i += nwg * blockDim.x)
+    ptr[(i / words) * stride + (i % words)] = 0u;
 }
 
 // Split-K partials of one attention row: chunk c holds (m_c, l_c) at ml[c * mstride] (running max in

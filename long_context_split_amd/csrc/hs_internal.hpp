@@ -113,6 +113,14 @@ hipError_t launch_attn_partial(const AttnArgs& a, int kvt, int ct, int nwr, bool
 // attn_wave: R <= 32 query rows per list, bf16 or FP8 caches, 8 independent waves per workgroup
 hipError_t launch_attn_wave(const AttnArgs& a, int kvt, bool gather, hipStream_t st);
 hipError_t launch_attn_merge(const MergeArgs& m, hipStream_t st);
+// attn_rows: dense pass 1 for R > 32 query rows per list, bf16 or FP8 caches, bf16 MFMA;
+// nrg = query-row groups of 32 per workgroup (2, 4 or 8; rows beyond 32*nrg take more z blocks)
+hipError_t launch_attn_rows(const AttnArgs& a, int kvt, int nrg, hipStream_t st);
+// attn_rows_scores: selection scores for R > 32 rows (G = 16 or a multiple of 32), bf16 or FP8;
+// a.hist (nullable) takes the first-digit histogram when a workgroup spans at most 4 query tokens
+hipError_t launch_attn_rows_scores(const ScoreArgs& a, int kvt, int nrg, hipStream_t st);
+int rows_groups(int R);
+int rows_tile_tokens(int nrg);
 hipError_t launch_attn_scores(const ScoreArgs& a, int kvt, int ct, int nwr, hipStream_t st);
 // fused_prefix: the histogram words were cleared and the first-digit histogram built by the
 // kernels before (attn_wave's zero hook, scores_wave); otherwise the select does both itself.

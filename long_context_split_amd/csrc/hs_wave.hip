@@ -31,14 +31,9 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Clears a strided set of words (caller-specified) with the whole grid.
+// Clears the words the caller asked for (the selection's histograms) with the whole grid.
 __device__ __forceinline__ void zero_hook(const AttnArgs& a) {
-  if (!a.zero_ptr) return;
-  const int64_t total = (int64_t)a.zero_lists * a.zero_words;
-  const int64_t nwg = (int64_t)gridDim.x * gridDim.y;
-  const int64_t wg = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-  for (int64_t i = wg * blockDim.x + threadIdx.x; i < total; i += nwg * blockDim.x)
-    a.zero_ptr[(i / a.zero_words) * a.zero_stride + (i % a.zero_words)] = 0u;
+  zero_words_grid(a.zero_ptr, a.zero_stride, a.zero_words, a.zero_lists);
 }
 
 }  // namespace
