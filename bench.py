@@ -219,7 +219,7 @@ def main():
     qps = queries / (ms * 1e-3)
 
     dom = max(kern.items(), key=lambda x: x[1]["total_ms_per_step"])[0] if kern else None
-    k1_name = "attn_wave_dense" if "attn_wave_dense" in kern else "attn_partial_dense"
+    k1_name = next((n for n in ("attn_wave_dense", "attn_rows_dense", "attn_partial_dense") if n in kern), None)
     k1 = kern.get(k1_name)
     k1_bytes = sum_L * row_bytes                                 # per launch (one block's full layer)
     # dense MFMA work of the pass: S = Q K^T and O = P V over every row, 2 * 2 * rows * L * d
