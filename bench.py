@@ -351,9 +351,39 @@ def bench_bridge(dev, iters):
     out_bytes = nt * 2 * T * (128 + 4)
     in_bytes = T * D * 2 + nt * 2 * D * 128 * 2
     log(f"bridge: {ms * 1e3:.1f} us  {tflops:.1f} TFLOP/s  ({tflops / 2500.0:.3f} of bf16 MFMA peak)")
+    # decode-time append: one new token per sequence of a 32-sequence batch, same weights and targets,
+    # each token to its own cache row
+    nb = 32
+    rows = torch.arange(nb, dtype=torch.int64) * 32768 + 1000
+    xa = x[:nb].contiguous()
+    for _ in range(3):
+        hs.kv_append(xa, wk, wv, tg, rows)
+    torch.cuda.synchronize()
+    h_rows = rows.numpy()
+    import ctypes
+    d_rows = rows.to(dev)
+    wkp = (ctypes.c_void_p * nt)(*[w.data_ptr() for w in wk])
+    wvp = (ctypes.c_void_p * nt)(*[w.data_ptr() for w in wv])
+    tgp = (ctypes.POINTER(hs.hs_kv_cache) * nt)(*[ctypes.pointer(t._c) for t in tg])
+    hrp = h_rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    stream = torch.cuda.current_stream().cuda_stream
+    aws = hs.workspace(hs.kv_append_workspace_size(nb, D, nt), dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in evs:
+        a.record()
+        hs.check(hs.lib.hs_kv_append(xa.data_ptr(), nb, D, nt, wkp, wvp, tgp, d_rows.data_ptr(), hrp,
+                                     aws.data_ptr(), aws.numel(), stream))
+        b.record()
+    torch.cuda.synchronize()
+    ms_app = statistics.median(a.elapsed_time(b) for a, b in evs)
+    app_bytes = nt * 2 * D * 128 * 2 + nb * D * 2 + nt * 2 * nb * (128 + 4)
+    log(f"kv append ({nb} tokens): {ms_app * 1e3:.1f} us  {app_bytes / (ms_app * 1e-3) / 1e9:.0f} GB/s")
     return {"workload": "c4_bridge_32k: X[32768,4096] bf16 x 4 targets (K,V) -> FP8 E4M3 + per-token scale",
             "ms": round(ms, 4), "tflops": round(tflops, 1), "bound": "mfma", "peak_tflops": 2500.0,
-            "frac": round(tflops / 2500.0, 4), "flops": flops, "bytes": in_bytes + out_bytes}
+            "frac": round(tflops / 2500.0, 4), "flops": flops, "bytes": in_bytes + out_bytes,
+            "decode_append": {"workload": f"{nb} new tokens x 4096 -> 4 targets (K,V), FP8, scattered rows",
+                              "us": round(ms_app * 1e3, 2), "bytes": app_bytes,
+                              "GBps": round(app_bytes / (ms_app * 1e-3) / 1e9, 1), "bound": "hbm (weights)"}}
 
 
 def cpu_baseline(case, spec, top_k, window, budget_s):

@@ -141,6 +141,32 @@ hs_status hs_kv_bridge(const void *hidden, int64_t n_tokens, int32_t d_model, in
                        const void *const *w_k, const void *const *w_v,
                        const hs_kv_cache *const *targets, int64_t row_offset, void *stream);
 
+/* Decode-time KV append through the bridge (ithome page, KV-sharing overview,
+ * and the prefill early-exit paragraphs: once generation starts the Cross-
+ * Decoder runs normally, so each new token's K/V for every target full layer
+ * is projected from the matching Self-Decoder hidden state).  Computes exactly
+ * what hs_kv_bridge computes for these n_tokens rows (same rounding and FP8
+ * scaling), but token t is stored at cache row rows[t] of every target instead
+ * of a contiguous range: for a decode step, rows[b] = row_start[b] + L_b of
+ * sequence b (the caller then advances its lengths).
+ *   hidden      device bf16 [n_tokens, d_model]
+ *   w_k, w_v, targets   as for hs_kv_bridge
+ *   d_rows      device int64 [n_tokens]: destination row of each token
+ *   h_rows      host int64 [n_tokens]: the same rows, used only to validate
+ *   workspace   device scratch of hs_kv_append_workspace_size() bytes (may be
+ *               NULL when that is 0); the library keeps nothing in it
+ * Up to 128 tokens the product is split over d_model (the weights dominate the
+ * bytes) and summed in a fixed order, so values may differ from hs_kv_bridge's
+ * in the last float32 bit before rounding; more tokens use the bridge kernel.
+ * Errors: HS_ERR_INVALID_ARGUMENT as for hs_kv_bridge, and for a row outside
+ * [0, capacity_rows) of any target or a row named twice (the writes would
+ * race); HS_ERR_WORKSPACE_TOO_SMALL. */
+size_t hs_kv_append_workspace_size(int64_t n_tokens, int32_t d_model, int32_t n_targets);
+hs_status hs_kv_append(const void *hidden, int64_t n_tokens, int32_t d_model, int32_t n_targets,
+                       const void *const *w_k, const void *const *w_v,
+                       const hs_kv_cache *const *targets, const int64_t *d_rows, const int64_t *h_rows,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
 /* Full-attention layer of a hybrid block, with token-level selection
  * (ithome page, "KV Reuse" section and recent-window paragraph; cnyes page
  * "檢索精確到token"; dpshk page section 03).  For every sequence b, query token t

@@ -252,6 +252,45 @@ void plan_sparse(const hs_kv_cache* kv, const hs_attn_params* p, hs_dtype q_dtyp
 
 }  // namespace
 
+namespace {
+
+// Shared by hs_kv_bridge and hs_kv_append: validates the targets and fills the launch arguments.
+// Rows are checked by the callers.
+hs_status bridge_args(const void* hidden, int64_t n_tokens, int32_t d_model, int32_t n_targets,
+                      const void* const* w_k, const void* const* w_v, const hs_kv_cache* const* targets,
+                      hs::BridgeArgs& a) {
+  if (!hidden || !w_k || !w_v || !targets) return fail(HS_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (n_tokens < 0) return fail(HS_ERR_INVALID_ARGUMENT, "n_tokens %lld", (long long)n_tokens);
+  if (d_model < 64 || d_model % 64) return fail(HS_ERR_INVALID_ARGUMENT, "d_model %d must be a positive multiple of 64", d_model);
+  if (n_targets < 1 || n_targets > 8) return fail(HS_ERR_UNSUPPORTED, "n_targets %d (1..8 supported)", n_targets);
+  if (!aligned16(hidden)) return fail(HS_ERR_INVALID_ARGUMENT, "hidden not 16-byte aligned");
+  int fp8 = -1;
+  for (int l = 0; l < n_targets; ++l) {
+    const hs_kv_cache* t = targets[l];
+    if (!t || !w_k[l] || !w_v[l]) return fail(HS_ERR_INVALID_ARGUMENT, "target %d: NULL pointer", l);
+    CacheInfo ci;
+    hs_status st = check_cache(t, ci, false);
+    if (st != HS_OK) return st;
+    if (t->dtype != HS_BF16 && t->dtype != HS_FP8_E4M3)
+      return fail(HS_ERR_INVALID_ARGUMENT, "target %d: bridge output must be BF16 or FP8_E4M3", l);
+    if (t->num_kv_heads != 1) return fail(HS_ERR_UNSUPPORTED, "target %d: bridge targets have one KV head", l);
+    const int f = t->dtype == HS_FP8_E4M3;
+    if (fp8 >= 0 && f != fp8) return fail(HS_ERR_UNSUPPORTED, "all targets of one call must share a dtype");
+    fp8 = f;
+    if (!aligned16(w_k[l]) || !aligned16(w_v[l])) return fail(HS_ERR_INVALID_ARGUMENT, "target %d: weights not 16-byte aligned", l);
+    a.w[2 * l] = (const uint16_t*)w_k[l];
+    a.w[2 * l + 1] = (const uint16_t*)w_v[l];
+    a.out[2 * l] = t->k;
+    a.out[2 * l + 1] = t->v;
+    a.scale[2 * l] = t->k_scale;
+    a.scale[2 * l + 1] = t->v_scale;
+  }
+  a.x = (const uint16_t*)hidden; a.T = n_tokens; a.Dm = d_model; a.n_targets = n_targets; a.fp8 = fp8;
+  return HS_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int hs_abi_version(void) { return HS_ABI_VERSION; }
@@ -510,42 +549,67 @@ hs_status hs_kv_bridge(const void* hidden, int64_t n_tokens, int32_t d_model, in
                        const void* const* w_k, const void* const* w_v, const hs_kv_cache* const* targets,
                        int64_t row_offset, void* stream) {
   g_last_error.clear();
-  if (!hidden || !w_k || !w_v || !targets) return fail(HS_ERR_INVALID_ARGUMENT, "NULL pointer argument");
-  if (n_tokens < 0) return fail(HS_ERR_INVALID_ARGUMENT, "n_tokens %lld", (long long)n_tokens);
-  if (d_model < 64 || d_model % 64) return fail(HS_ERR_INVALID_ARGUMENT, "d_model %d must be a positive multiple of 64", d_model);
-  if (n_targets < 1 || n_targets > 8) return fail(HS_ERR_UNSUPPORTED, "n_targets %d (1..8 supported)", n_targets);
-  if (row_offset < 0) return fail(HS_ERR_INVALID_ARGUMENT, "row_offset %lld", (long long)row_offset);
-  if (!aligned16(hidden)) return fail(HS_ERR_INVALID_ARGUMENT, "hidden not 16-byte aligned");
   hs::BridgeArgs a{};
-  int fp8 = -1;
-  for (int l = 0; l < n_targets; ++l) {
-    const hs_kv_cache* t = targets[l];
-    if (!t || !w_k[l] || !w_v[l]) return fail(HS_ERR_INVALID_ARGUMENT, "target %d: NULL pointer", l);
-    CacheInfo ci;
-    hs_status st = check_cache(t, ci, false);
-    if (st != HS_OK) return st;
-    if (t->dtype != HS_BF16 && t->dtype != HS_FP8_E4M3)
-      return fail(HS_ERR_INVALID_ARGUMENT, "target %d: bridge output must be BF16 or FP8_E4M3", l);
-    if (t->num_kv_heads != 1) return fail(HS_ERR_UNSUPPORTED, "target %d: bridge targets have one KV head", l);
-    const int f = t->dtype == HS_FP8_E4M3;
-    if (fp8 >= 0 && f != fp8) return fail(HS_ERR_UNSUPPORTED, "all targets of one call must share a dtype");
-    fp8 = f;
-    if (row_offset + n_tokens > t->capacity_rows)
+  hs_status st = bridge_args(hidden, n_tokens, d_model, n_targets, w_k, w_v, targets, a);
+  if (st != HS_OK) return st;
+  if (row_offset < 0) return fail(HS_ERR_INVALID_ARGUMENT, "row_offset %lld", (long long)row_offset);
+  for (int l = 0; l < n_targets; ++l)
+    if (row_offset + n_tokens > targets[l]->capacity_rows)
       return fail(HS_ERR_INVALID_ARGUMENT, "target %d: rows [%lld, %lld) exceed capacity %lld", l,
-                  (long long)row_offset, (long long)(row_offset + n_tokens), (long long)t->capacity_rows);
-    if (!aligned16(w_k[l]) || !aligned16(w_v[l])) return fail(HS_ERR_INVALID_ARGUMENT, "target %d: weights not 16-byte aligned", l);
-    a.w[2 * l] = (const uint16_t*)w_k[l];
-    a.w[2 * l + 1] = (const uint16_t*)w_v[l];
-    a.out[2 * l] = t->k;
-    a.out[2 * l + 1] = t->v;
-    a.scale[2 * l] = t->k_scale;
-    a.scale[2 * l + 1] = t->v_scale;
-  }
+                  (long long)row_offset, (long long)(row_offset + n_tokens), (long long)targets[l]->capacity_rows);
   if (n_tokens == 0) return HS_OK;
-  a.x = (const uint16_t*)hidden; a.T = n_tokens; a.Dm = d_model; a.n_targets = n_targets; a.fp8 = fp8;
   a.row_offset = row_offset;
   hipError_t e = timed("kv_bridge", (hipStream_t)stream, [&] { return hs::launch_bridge(a, (hipStream_t)stream); });
   if (e != hipSuccess) return hip_fail(e, "kv bridge");
+  return HS_OK;
+}
+
+size_t hs_kv_append_workspace_size(int64_t n_tokens, int32_t d_model, int32_t n_targets) {
+  if (n_tokens < 1 || n_tokens > hs::APPEND_MAX_TOKENS || d_model < 64 || d_model % 64 || n_targets < 1 ||
+      n_targets > 8)
+    return 0;
+  hs::AppendArgs ap{};
+  hs::append_plan(n_tokens, d_model, n_targets, ap);
+  return hs::append_workspace_bytes(ap);
+}
+
+hs_status hs_kv_append(const void* hidden, int64_t n_tokens, int32_t d_model, int32_t n_targets,
+                       const void* const* w_k, const void* const* w_v, const hs_kv_cache* const* targets,
+                       const int64_t* d_rows, const int64_t* h_rows, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  g_last_error.clear();
+  hs::BridgeArgs a{};
+  hs_status st = bridge_args(hidden, n_tokens, d_model, n_targets, w_k, w_v, targets, a);
+  if (st != HS_OK) return st;
+  if (n_tokens > 0 && (!d_rows || !h_rows)) return fail(HS_ERR_INVALID_ARGUMENT, "d_rows / h_rows is NULL");
+  int64_t cap = INT64_MAX;
+  for (int l = 0; l < n_targets; ++l) cap = std::min<int64_t>(cap, targets[l]->capacity_rows);
+  std::vector<int64_t> sorted(h_rows, h_rows + n_tokens);
+  std::sort(sorted.begin(), sorted.end());
+  for (int64_t i = 0; i < n_tokens; ++i) {
+    if (sorted[i] < 0 || sorted[i] >= cap)
+      return fail(HS_ERR_INVALID_ARGUMENT, "row %lld outside [0, %lld)", (long long)sorted[i], (long long)cap);
+    if (i && sorted[i] == sorted[i - 1])
+      return fail(HS_ERR_INVALID_ARGUMENT, "row %lld named twice", (long long)sorted[i]);
+  }
+  if (n_tokens == 0) return HS_OK;
+  hipError_t e;
+  if (n_tokens <= hs::APPEND_MAX_TOKENS) {
+    hs::AppendArgs ap{};
+    hs::append_plan(n_tokens, d_model, n_targets, ap);
+    const size_t need = hs::append_workspace_bytes(ap);
+    if (!workspace) return fail(HS_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    if (workspace_bytes < need)
+      return fail(HS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+    if (!aligned16(workspace)) return fail(HS_ERR_INVALID_ARGUMENT, "workspace not 16-byte aligned");
+    ap.x = a.x; ap.T = n_tokens; ap.Dm = d_model; ap.fp8 = a.fp8; ap.rows = d_rows; ap.part = (float*)workspace;
+    for (int i = 0; i < 2 * n_targets; ++i) { ap.w[i] = a.w[i]; ap.out[i] = a.out[i]; ap.scale[i] = a.scale[i]; }
+    e = timed("kv_append", (hipStream_t)stream, [&] { return hs::launch_append(ap, (hipStream_t)stream); });
+  } else {
+    a.rows = d_rows;
+    e = timed("kv_append", (hipStream_t)stream, [&] { return hs::launch_bridge(a, (hipStream_t)stream); });
+  }
+  if (e != hipSuccess) return hip_fail(e, "kv append");
   return HS_OK;
 }
 

@@ -103,7 +103,8 @@ __global__ __launch_bounds__(NT, 2) void bridge_kernel(BridgeArgs a) {
   // ---- epilogue: this wave holds rows 64 wm + [0, 64) of head block (tgt, wn)
   const int blk = 2 * tgt + wn;
   char* const ep = smem + wave * (64 * 128 * 2);
-  const int64_t orow0 = a.row_offset + m0 + 64 * wm;
+  const int64_t t0 = m0 + 64 * wm;                               // first token of this wave's rows
+  auto orow = [&](int rl) -> int64_t { return a.rows ? a.rows[t0 + rl] : a.row_offset + t0 + rl; };
   if (a.fp8) {
     float* sc = a.scale[blk];
 #pragma unroll
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(NT, 2) void bridge_kernel(BridgeArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           ep[rl * 128 + 32 * j + (lane & 31)] = (char)f32_to_e4m3_rne(acc[i][j][r] / scale);
-        if ((lane & 31) == 0 && m0 + 64 * wm + rl < a.T) sc[orow0 + rl] = scale;
+        if ((lane & 31) == 0 && t0 + rl < a.T) sc[orow(rl)] = scale;
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(NT, 2) void bridge_kernel(BridgeArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int p = lane + 64 * i, rl = p >> 3, c = p & 7;
-      if (m0 + 64 * wm + rl < a.T) *(u32x4*)(dst + (orow0 + rl) * 128 + c * 16) = *(const u32x4*)(ep + rl * 128 + c * 16);
+      if (t0 + rl < a.T) *(u32x4*)(dst + orow(rl) * 128 + c * 16) = *(const u32x4*)(ep + rl * 128 + c * 16);
     }
   } else {
     uint16_t* e16 = (uint16_t*)ep;
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(NT, 2) void bridge_kernel(BridgeArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int p = lane + 64 * i, rl = p >> 4, c = p & 15;
-      if (m0 + 64 * wm + rl < a.T) *(u32x4*)(dst + (orow0 + rl) * 256 + c * 16) = *(const u32x4*)(ep + rl * 256 + c * 16);
+      if (t0 + rl < a.T) *(u32x4*)(dst + orow(rl) * 256 + c * 16) = *(const u32x4*)(ep + rl * 256 + c * 16);
     }
   }
 }

@@ -103,7 +103,27 @@ struct BridgeArgs {
   float* scale[16];      // per block: FP8 scale base pointer or null
   int fp8;
   int64_t row_offset;
+  const int64_t* rows;   // nullable: cache row of each token (decode-time append); else row_offset + t
 };
+
+// Decode-time append (few tokens): split-K partials in a caller workspace, then a finish kernel.
+struct AppendArgs {
+  const uint16_t* x;     // [T, Dm] bf16
+  int64_t T;
+  int Dm;
+  int n_blocks;          // 2 * n_targets head blocks (target, K|V) of 128 columns
+  int n_slices, m_tiles;
+  const uint16_t* w[16];
+  void* out[16];
+  float* scale[16];
+  int fp8;
+  const int64_t* rows;   // cache row of each token
+  float* part;           // workspace: [n_slices][n_blocks][m_tiles][32][128] float32
+};
+void append_plan(int64_t n_tokens, int d_model, int n_targets, AppendArgs& a);
+size_t append_workspace_bytes(const AppendArgs& a);
+hipError_t launch_append(const AppendArgs& a, hipStream_t st);
+constexpr int64_t APPEND_MAX_TOKENS = 128;   // above this hs_kv_append uses the bridge kernel
 
 int rows_per_wave_group(int R);
 int partial_tile_tokens(int nwr);

@@ -87,6 +87,12 @@ lib.hs_select_from_scores.argtypes = [_P, _P, ctypes.POINTER(ctypes.c_int32)] + 
 lib.hs_kv_bridge.restype = ctypes.c_int
 lib.hs_kv_bridge.argtypes = [_P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_P),
                              ctypes.POINTER(_P), ctypes.POINTER(_KVP), ctypes.c_int64, _P]
+lib.hs_kv_append.restype = ctypes.c_int
+lib.hs_kv_append.argtypes = [_P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_P),
+                             ctypes.POINTER(_P), ctypes.POINTER(_KVP), _P, ctypes.POINTER(ctypes.c_int64), _P,
+                             ctypes.c_size_t, _P]
+lib.hs_kv_append_workspace_size.restype = ctypes.c_size_t
+lib.hs_kv_append_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
 
 class hs_kernel_time(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char_p), ("ms", ctypes.c_float)]
@@ -275,6 +281,27 @@ def kv_bridge(hidden, w_k, w_v, targets, row_offset, stream=None):
     tg = (_KVP * n)(*[ctypes.pointer(t._c) for t in targets])
     check(lib.hs_kv_bridge(_ptr(hidden), hidden.shape[0], hidden.shape[1], n, wk, wv, tg, int(row_offset),
                            _stream(stream)))
+
+
+def kv_append_workspace_size(n_tokens, d_model, n_targets):
+    return lib.hs_kv_append_workspace_size(n_tokens, d_model, n_targets)
+
+
+def kv_append(hidden, w_k, w_v, targets, rows, ws=None, stream=None):
+    """Decode-time append: token t of hidden [n, Dm] bf16 goes to cache row rows[t] of every target.
+    rows: int64 sequence or device tensor; both a device and a host copy are passed."""
+    h_rows = np.ascontiguousarray(np.asarray(rows.cpu() if isinstance(rows, torch.Tensor) else rows, np.int64))
+    d_rows = torch.from_numpy(h_rows).to(hidden.device)
+    n = len(targets)
+    if ws is None:
+        ws = workspace(kv_append_workspace_size(hidden.shape[0], hidden.shape[1], n), hidden.device)
+    wk = (ctypes.c_void_p * n)(*[w.data_ptr() for w in w_k])
+    wv = (ctypes.c_void_p * n)(*[w.data_ptr() for w in w_v])
+    tg = (_KVP * n)(*[ctypes.pointer(t._c) for t in targets])
+    check(lib.hs_kv_append(_ptr(hidden), hidden.shape[0], hidden.shape[1], n, wk, wv, tg, _ptr(d_rows),
+                           h_rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _ptr(ws), ws.numel(),
+                           _stream(stream)))
+    return d_rows
 
 
 def timing_enable(on=True):

@@ -143,3 +143,30 @@ def test_bridge_rejects(hs):
     assert f(None, 100, 4096, 1, w, w, tp, 0, None) == 1
     assert f(0x900000, 100, 4096, 9, w, w, tp, 0, None) == 2
     assert f(0x900000, 0, 4096, 1, w, w, tp, 0, None) == 0            # nothing to do: no launch
+
+
+def test_append_rejects(hs):
+    t = _cache(hs, dtype=2, scales=True, lens=(1,), cap=1000)
+    tp = (ctypes.POINTER(hs.hs_kv_cache) * 1)(ctypes.pointer(t))
+    w = (ctypes.c_void_p * 1)(0x800000)
+    f = hs.lib.hs_kv_append
+
+    def rows(*r):
+        a = np.asarray(r, np.int64)
+        return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+    big = 1 << 20
+    a, p = rows(3, 999, 1000)
+    assert f(0x900000, 3, 4096, 1, w, w, tp, 0xA00000, p, 0xB00000, big, None) == 1   # row 1000 outside capacity
+    a, p = rows(3, -1)
+    assert f(0x900000, 2, 4096, 1, w, w, tp, 0xA00000, p, 0xB00000, big, None) == 1   # negative row
+    a, p = rows(5, 7, 5)
+    assert f(0x900000, 3, 4096, 1, w, w, tp, 0xA00000, p, 0xB00000, big, None) == 1   # row named twice
+    a, p = rows(5, 7)
+    assert f(0x900000, 2, 4096, 1, w, w, tp, None, p, 0xB00000, big, None) == 1       # no device rows
+    assert f(0x900000, 2, 4000, 1, w, w, tp, 0xA00000, p, 0xB00000, big, None) == 1   # d_model not a multiple of 64
+    need = hs.lib.hs_kv_append_workspace_size(2, 4096, 1)
+    assert need > 0
+    assert f(0x900000, 2, 4096, 1, w, w, tp, 0xA00000, p, 0xB00000, need - 16, None) == 3   # workspace too small
+    assert f(0x900000, 2, 4096, 1, w, w, tp, 0xA00000, p, None, 0, None) == 1          # no workspace
+    assert f(0x900000, 0, 4096, 1, w, w, tp, None, None, None, 0, None) == 0           # nothing to do: no launch

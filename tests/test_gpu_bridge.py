@@ -140,3 +140,36 @@ def test_config4_full_size_sampled_rows():
     frac = _check_random(case, tg, spec["offset"], True, rows)
     assert frac >= 0.99
     print(f"[result] bridge config4 equal fraction {frac:.5f}", flush=True)
+
+
+@pytest.mark.parametrize("fp8", [True, False])
+@pytest.mark.parametrize("n", [1, 37, 128, 150])
+def test_decode_append_scattered_rows(fp8, n):
+    """Decode-time append: token t of the step lands at cache row rows[t] of every target, with the
+    values the oracle projects and stores (the same bounds as the contiguous bridge; up to 128 tokens
+    the split-over-d_model kernels run, above that the bridge kernel with a row map); every other
+    row is untouched."""
+    banner(f"kv append n={n} fp8={fp8}")
+    from long_context_split_amd import hysparse as hs
+    case = synth.bridge_case(4, T=n, D=512, n_targets=2)
+    cap = 700
+    rows = np.random.default_rng(42 + n).choice(cap, n, replace=False).astype(np.int64)
+    tg = _targets(2, cap, fp8)
+    hs.kv_append(dev_bf16(case["x"]), [dev_bf16(w) for w in case["w_k"]], [dev_bf16(w) for w in case["w_v"]],
+                 tg, rows)
+    torch.cuda.synchronize()
+    others = np.setdiff1d(np.arange(cap), rows)
+    for t in tg:
+        k, ks, v, vs = _host(t, fp8)
+        sent = SENT8 if fp8 else 0x1234
+        assert np.all(k[others] == sent) and np.all(v[others] == sent)
+        if fp8:
+            assert np.all(ks[others] == SENTF) and np.all(vs[others] == SENTF)
+    # gather the appended rows into contiguous views and hold them to the bridge's oracle bounds
+    class _View:
+        def __init__(self, t):
+            self.k, self.v = t.k[torch.from_numpy(rows).cuda()], t.v[torch.from_numpy(rows).cuda()]
+            self.k_scale = t.k_scale[torch.from_numpy(rows).cuda()] if fp8 else None
+            self.v_scale = t.v_scale[torch.from_numpy(rows).cuda()] if fp8 else None
+    frac = _check_random(case, [_View(t) for t in tg], 0, fp8)
+    assert frac >= 0.99
