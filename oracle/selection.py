@@ -85,3 +85,78 @@ def select_all(s, L, top_k, window, f32_keys=False):
         for g in range(n_kv):
             idx[t, g], cnt[t, g] = select(s[t, g], L, top_k, window, f32_keys)
     return idx, cnt
+
+
+# ---------------------------------------------------------------- HySparse v1 block-level variant
+#
+# dpshk page, section 03, and the cnyes page, section "檢索精確到token": the previous
+# HySparse generation chose history in blocks of 64 tokens, so a block with one useful token
+# still spent 64 positions of the budget.  Readings taken where the pages are silent:
+# * the same scores s_j as the token-level selection, over the same candidates [0, L - W');
+# * block b covers candidates [64 b, min(64 b + 64, n)); its score is the sum of its
+#   tokens' scores (the block's share of the attention mass);
+# * the same token budget: when k' < n, floor(k' / 64) whole blocks are chosen (block
+#   score descending, ties to the lower block); when k' >= n every candidate is chosen;
+# * emitted list: the chosen blocks' tokens in ascending order, then the window, then -1;
+#   count = chosen tokens + W'.
+
+BLOCK = 64
+
+
+def f32_tree_sum(x):
+    """float32 sum of the rows of x [m, 2^p] as a balanced pairwise tree in index order:
+    (x0 + x1) + (x2 + x3) ..., every addition rounded to float32.  This is the fixed order in
+    which the library's block pooling adds a block's scores, so that tests can take the
+    integer block ranking in the same precision on both sides."""
+    v = np.ascontiguousarray(x, dtype=np.float32)
+    while v.shape[1] > 1:
+        v = (v[:, 0::2] + v[:, 1::2]).astype(np.float32)
+    return v[:, 0]
+
+
+def block_scores(scores, block=BLOCK, f32_tree=False):
+    """Per-block sums of the candidate scores; the last block may be partial (zeros pad it)."""
+    s = np.asarray(scores)
+    n = s.shape[0]
+    nb = (n + block - 1) // block
+    pad = np.zeros(nb * block, dtype=np.float32 if f32_tree else np.float64)
+    pad[:n] = s
+    m = pad.reshape(nb, block)
+    return f32_tree_sum(m) if f32_tree else m.sum(axis=1)
+
+
+def select_blocks(scores, L, top_k, window, block=BLOCK, f32_tree=False):
+    """Block-level selection list of one (token, KV head): (idx int32 [window + top_k], count).
+    f32_tree: block sums in the float32 tree order above, ranked by their float32 key order
+    (scores must then be float32)."""
+    w, kk = budget(L, top_k, window)
+    n = int(L) - w
+    s = np.asarray(scores)
+    if s.shape != (n,):
+        raise ValueError(f"expected {n} candidate scores, got {s.shape}")
+    cap = int(window) + int(top_k)
+    out = np.full(cap, -1, dtype=np.int32)
+    if kk >= n:
+        glob = np.arange(n, dtype=np.int64)
+    else:
+        bs = block_scores(s, block, f32_tree)
+        key = f32_key(bs).astype(np.int64) if f32_tree else bs.astype(np.float64)
+        chosen = _top_global(key, kk // block)             # ascending block indices
+        glob = np.concatenate([np.arange(b * block, min(b * block + block, n)) for b in chosen]) \
+            if len(chosen) else np.zeros(0, dtype=np.int64)
+    g = len(glob)
+    out[:g] = glob
+    out[g:g + w] = np.arange(int(L) - w, int(L), dtype=np.int32)
+    return out, g + w
+
+
+def select_blocks_all(s, L, top_k, window, block=BLOCK, f32_tree=False):
+    """select_blocks() over s [n_q, n_kv, L - W'] -> (idx [n_q, n_kv, C], count [n_q, n_kv])."""
+    n_q, n_kv, _ = s.shape
+    cap = int(window) + int(top_k)
+    idx = np.empty((n_q, n_kv, cap), dtype=np.int32)
+    cnt = np.empty((n_q, n_kv), dtype=np.int32)
+    for t in range(n_q):
+        for g in range(n_kv):
+            idx[t, g], cnt[t, g] = select_blocks(s[t, g], L, top_k, window, block, f32_tree)
+    return idx, cnt
