@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define HS_ABI_VERSION 1
+#define HS_ABI_VERSION 2
 
 typedef enum {
   HS_OK = 0,
@@ -97,6 +97,17 @@ typedef struct {
  *   top_k         global budget k (1024 in the pages), taken from outside the window
  *   window        recent window W (128 in the pages), always selected
  *   softmax_scale 0 => 1/sqrt(head_dim)
+ *   select_block  0 (or 1): token-level selection, the HySparse2 mechanism;
+ *                 64: the previous generation's block-level selection (dpshk
+ *                 page, section 03: history chosen in 64-token blocks), kept
+ *                 as a comparison variant.  Block b covers candidates
+ *                 [64b, min(64b + 64, L - W')); its score is the float32 sum of
+ *                 its tokens' scores added as a pairwise tree in index order;
+ *                 when k' < L - W' the list takes floor(k'/64) whole blocks
+ *                 (score descending, ties to the lower block), else every
+ *                 candidate; global tokens ascending, then the window, then -1.
+ *                 Other values: HS_ERR_UNSUPPORTED.  Only hs_full_attn_select
+ *                 reads it.
  * ithome page, recent-window paragraph: the 128 most recent tokens are forced
  * into the selection and 1,024 global tokens come from outside that window. */
 typedef struct {
@@ -105,6 +116,7 @@ typedef struct {
   int32_t top_k;
   int32_t window;
   float softmax_scale;
+  int32_t select_block;
 } hs_attn_params;
 
 /* Workspace bytes hs_full_attn_select needs for these shapes (0 on invalid
@@ -216,13 +228,13 @@ hs_status hs_sparse_attn(const hs_kv_cache *kv, const hs_attn_params *p, const v
  * [batch, q_tokens, n_kv, max_len - min(window, max_len)] laid out as
  * scores_out above; lists with L_b = d_seq_len[b] use their first
  * L_b - min(window, L_b) entries.  Scores must be finite; the order is the
- * float order (-0 below +0), ties to the lower index.  Outputs as
- * hs_full_attn_select. */
+ * float order (-0 below +0), ties to the lower index.  select_block as in
+ * hs_attn_params (0: tokens, 64: blocks).  Outputs as hs_full_attn_select. */
 hs_status hs_select_from_scores(const float *scores, const int32_t *d_seq_len,
                                 const int32_t *h_seq_len, int32_t batch, int32_t q_tokens,
                                 int32_t n_kv, int32_t max_len, int32_t top_k, int32_t window,
-                                int32_t *sel_idx, int32_t *sel_count, void *workspace,
-                                size_t workspace_bytes, void *stream);
+                                int32_t select_block, int32_t *sel_idx, int32_t *sel_count,
+                                void *workspace, size_t workspace_bytes, void *stream);
 
 /* Kernel timing, a profiling aid (off by default).  While enabled, every
  * kernel the library enqueues is bracketed by a pair of HIP events recorded on

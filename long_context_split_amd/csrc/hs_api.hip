@@ -132,6 +132,16 @@ hs_status check_params(const hs_attn_params* p, int n_kv) {
     return fail(HS_ERR_INVALID_ARGUMENT, "top_k %d / window %d", p->top_k, p->window);
   if (!(p->softmax_scale >= 0.f) || !isfinite(p->softmax_scale))
     return fail(HS_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
+  if (p->select_block != 0 && p->select_block != 1 && p->select_block != 64)
+    return fail(HS_ERR_UNSUPPORTED, "select_block %d (0, 1 or 64)", p->select_block);
+  return HS_OK;
+}
+
+// block-level selection keeps a list's block keys in LDS
+hs_status check_block_select(int select_block, int64_t max_cand) {
+  if (select_block == 64 && max_cand > hs::select_blocks_max_candidates())
+    return fail(HS_ERR_UNSUPPORTED, "block-level selection supports at most %lld candidates per list",
+                (long long)hs::select_blocks_max_candidates());
   return HS_OK;
 }
 
@@ -369,6 +379,7 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
   if (!aligned16(q)) return fail(HS_ERR_INVALID_ARGUMENT, "q not 16-byte aligned");
   FullPlan pl;
   if ((st = plan_full(kv, p, q_dtype, ci, pl)) != HS_OK) return st;
+  if ((st = check_block_select(p->select_block, pl.s_stride)) != HS_OK) return st;
   if (!workspace && pl.total) return fail(HS_ERR_INVALID_ARGUMENT, "workspace is NULL");
   if (workspace_bytes < pl.total)
     return fail(HS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, pl.total);
@@ -455,8 +466,11 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
   se.sel_idx = sel_idx; se.sel_count = sel_count;
   se.ws = (uint32_t*)(ws + pl.off_sel); se.ws_stride = pl.sel.ws_stride; se.cand_off = pl.sel.cand_off;
   se.chunk = pl.sel.chunk; se.max_chunks = pl.sel.max_chunks;
-  if ((e = timed("select_topk", s, [&] { return hs::launch_select(se, n_sel_lists, fused_prefix, s); })) != hipSuccess)
-    return hip_fail(e, "selection");
+  if (p->select_block == 64)
+    e = timed("select_blocks", s, [&] { return hs::launch_select_blocks(se, n_sel_lists, pl.s_stride, s); });
+  else
+    e = timed("select_topk", s, [&] { return hs::launch_select(se, n_sel_lists, fused_prefix, s); });
+  if (e != hipSuccess) return hip_fail(e, "selection");
   return HS_OK;
 }
 
@@ -514,8 +528,8 @@ hs_status hs_sparse_attn(const hs_kv_cache* kv, const hs_attn_params* p, const v
 
 hs_status hs_select_from_scores(const float* scores, const int32_t* d_seq_len, const int32_t* h_seq_len,
                                 int32_t batch, int32_t q_tokens, int32_t n_kv, int32_t max_len, int32_t top_k,
-                                int32_t window, int32_t* sel_idx, int32_t* sel_count, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+                                int32_t window, int32_t select_block, int32_t* sel_idx, int32_t* sel_count,
+                                void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   if (!scores || !d_seq_len || !h_seq_len || !sel_idx || !sel_count)
     return fail(HS_ERR_INVALID_ARGUMENT, "NULL pointer argument");
@@ -526,6 +540,10 @@ hs_status hs_select_from_scores(const float* scores, const int32_t* d_seq_len, c
   for (int b = 0; b < batch; ++b)
     if (h_seq_len[b] < 1 || h_seq_len[b] > max_len)
       return fail(HS_ERR_INVALID_ARGUMENT, "seq_len[%d] = %d outside [1, max_len]", b, h_seq_len[b]);
+  if (select_block != 0 && select_block != 1 && select_block != 64)
+    return fail(HS_ERR_UNSUPPORTED, "select_block %d (0, 1 or 64)", select_block);
+  hs_status bst = check_block_select(select_block, max_len - std::min(window, max_len));
+  if (bst != HS_OK) return bst;
   const size_t need = hs_select_workspace_size(batch, q_tokens, n_kv, max_len, top_k, window);
   if (!workspace) return fail(HS_ERR_INVALID_ARGUMENT, "workspace is NULL");
   if (workspace_bytes < need)
@@ -539,8 +557,12 @@ hs_status hs_select_from_scores(const float* scores, const int32_t* d_seq_len, c
   hs::select_plan(se.s_stride, sp);
   se.ws = (uint32_t*)workspace; se.ws_stride = sp.ws_stride; se.cand_off = sp.cand_off;
   se.chunk = sp.chunk; se.max_chunks = sp.max_chunks;
-  hipError_t e = timed("select_topk", (hipStream_t)stream,
-                       [&] { return hs::launch_select(se, batch * q_tokens * n_kv, false, (hipStream_t)stream); });
+  const int n_lists = batch * q_tokens * n_kv;
+  hipError_t e = select_block == 64
+                     ? timed("select_blocks", (hipStream_t)stream,
+                             [&] { return hs::launch_select_blocks(se, n_lists, se.s_stride, (hipStream_t)stream); })
+                     : timed("select_topk", (hipStream_t)stream,
+                             [&] { return hs::launch_select(se, n_lists, false, (hipStream_t)stream); });
   if (e != hipSuccess) return hip_fail(e, "selection");
   return HS_OK;
 }

@@ -145,6 +145,9 @@ hipError_t launch_attn_scores(const ScoreArgs& a, int kvt, int ct, int nwr, hipS
 // fused_prefix: the histogram words were cleared and the first-digit histogram built by the
 // kernels before (attn_wave's zero hook, scores_wave); otherwise the select does both itself.
 hipError_t launch_select(const SelectArgs& a, int n_lists, bool fused_prefix, hipStream_t st);
+// block-level variant (64-token blocks); max_cand = the longest list's candidate count
+hipError_t launch_select_blocks(const SelectArgs& a, int n_lists, int64_t max_cand, hipStream_t st);
+int64_t select_blocks_max_candidates();
 hipError_t launch_scores_wave(const ScoreArgs& a, int kvt, hipStream_t st);
 constexpr int SELECT_ZERO_WORDS = 4100;   // per-list words the selection needs cleared
 hipError_t launch_bridge(const BridgeArgs& a, hipStream_t st);

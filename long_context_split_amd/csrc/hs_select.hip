@@ -337,6 +337,111 @@ __global__ __launch_bounds__(CH_NT) void sel_write_kernel(SelectArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- block-level variant (HySparse v1)
+//
+// dpshk page, section 03: the previous generation chose history in 64-token blocks.  Block b
+// covers candidates [64 b, min(64 b + 64, n)); its score is the sum of its tokens' scores, added
+// as a balanced pairwise tree in index order in float32 (a wave butterfly); the budget k' buys
+// floor(k' / 64) whole blocks (score descending, ties to the lower block) unless k' >= n, when
+// every candidate is taken.  Block scores live in the candidate area of the list's workspace.
+
+constexpr int BLK = 64;
+constexpr int MAX_BLOCKS = 32768;              // block keys of one list held in LDS
+
+__global__ __launch_bounds__(256) void sel_block_pool_kernel(SelectArgs a) {
+  const int list = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int blk = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const ListInfo li = list_info(a, list);
+  if (li.kk == 0 || li.kk >= li.n) return;                       // nothing to rank
+  if (blk >= (li.n + BLK - 1) / BLK) return;
+  const int j = blk * BLK + lane;
+  float v = j < li.n ? a.scores[(size_t)list * a.s_stride + j] : 0.f;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);       // same tree on every lane
+  if (lane == 0) ws_list(a, list)[a.cand_off + blk] = f32_key(v);
+}
+
+__global__ __launch_bounds__(FIN_NT) void sel_block_select_kernel(SelectArgs a) {
+  __shared__ uint32_t key[MAX_BLOCKS];
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t sh[3 * (FIN_NT / 64) + 3];
+  __shared__ int s_last_taken;
+  const int list = blockIdx.x;
+  const ListInfo li = list_info(a, list);
+  int32_t* out = a.sel_idx + (size_t)list * a.cap;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_last_taken = 0;
+  int g = 0;                                                      // global tokens emitted
+  if (li.kk >= li.n) {
+    for (int i = tid; i < li.n; i += FIN_NT) out[i] = i;
+    g = li.n;
+  } else if (li.kk / BLK > 0) {
+    const int nb = (li.n + BLK - 1) / BLK, kb = li.kk / BLK;
+    const uint32_t* wk = ws_list(a, list) + a.cand_off;
+    for (int b = tid; b < nb; b += FIN_NT) key[b] = wk[b];
+    // exact kb-th largest key T over three digits (11, 11, 10 bits), and `need` keys == T taken
+    uint32_t prefix = 0, rem = (uint32_t)kb;
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
+      const uint32_t bins = pass == 2 ? 1024u : 2048u;
+      const uint32_t hmask = pass == 0 ? 0u : pass == 1 ? 0xFFE00000u : 0xFFFFFC00u;
+      for (int i = tid; i < 2048; i += FIN_NT) hist[i] = 0u;
+      __syncthreads();
+      for (int b = tid; b < nb; b += FIN_NT)
+        if ((key[b] & hmask) == prefix) atomicAdd(&hist[(key[b] >> shift) & (bins - 1)], 1u);
+      __syncthreads();
+      uint32_t d;
+      if (pass == 2) find_digit<FIN_NT, 1024>(hist, rem, sh, d, rem);
+      else find_digit<FIN_NT, 2048>(hist, rem, sh, d, rem);
+      prefix |= d << shift;
+    }
+    const uint32_t T = prefix, need = rem;
+    // contiguous blocks per thread, so scans follow block order
+    const int per = (nb + FIN_NT - 1) / FIN_NT;
+    const int b0 = min(nb, tid * per), b1 = min(nb, b0 + per);
+    uint32_t ties = 0;
+    for (int b = b0; b < b1; ++b) ties += key[b] == T;
+    uint32_t tot;
+    uint32_t tie_rank = block_scan_excl<FIN_NT>(ties, sh, tot, false);
+    uint32_t mine = 0;
+    for (int b = b0; b < b1; ++b) {
+      const uint32_t k = key[b];
+      if (k > T) ++mine;
+      else if (k == T) mine += tie_rank++ < need;
+    }
+    uint32_t nsel;
+    uint32_t slot = block_scan_excl<FIN_NT>(mine, sh, nsel, false);
+    tie_rank -= ties;                                             // back to this thread's first tie
+    for (int b = b0; b < b1; ++b) {
+      const uint32_t k = key[b];
+      bool take = k > T;
+      if (k == T) take = tie_rank++ < need;
+      if (!take) continue;
+      const int j1 = min(b * BLK + BLK, li.n);
+      for (int j = b * BLK; j < j1; ++j) out[slot * BLK + (j - b * BLK)] = j;
+      ++slot;
+      if (b == nb - 1) s_last_taken = 1;
+    }
+    __syncthreads();
+    // only the last block can be partial, and it is the last one emitted when chosen
+    g = (int)nsel * BLK - (s_last_taken ? nb * BLK - li.n : 0);
+  }
+  __syncthreads();
+  for (int i = tid; i < li.w; i += FIN_NT) out[g + i] = li.n + i;   // window rows L-W' .. L-1
+  for (int i = g + li.w + tid; i < a.cap; i += FIN_NT) out[i] = -1;
+  if (tid == 0) a.sel_count[list] = g + li.w;
+}
+
+hipError_t launch_select_blocks(const SelectArgs& a, int n_lists, int64_t max_cand, hipStream_t st) {
+  const int nb_max = (int)((max_cand + BLK - 1) / BLK);
+  if (nb_max > 0) hipLaunchKernelGGL(sel_block_pool_kernel, dim3((nb_max + 3) / 4, n_lists), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(sel_block_select_kernel, dim3(n_lists), dim3(FIN_NT), 0, st, a);
+  return hipGetLastError();
+}
+
+int64_t select_blocks_max_candidates() { return (int64_t)MAX_BLOCKS * BLK; }
+
 static_assert(W_ZERO == SELECT_ZERO_WORDS, "cleared words of the selection workspace");
 
 hipError_t launch_select(const SelectArgs& a, int n_lists, bool fused_prefix, hipStream_t st) {

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libhysparse.so")
 
 HS_OK, HS_ERR_INVALID_ARGUMENT, HS_ERR_UNSUPPORTED, HS_ERR_WORKSPACE_TOO_SMALL, HS_ERR_HIP = range(5)
 HS_F32, HS_BF16, HS_FP8_E4M3 = 0, 1, 2
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class HsError(RuntimeError):
@@ -61,6 +61,7 @@ class hs_attn_params(ctypes.Structure):
         ("top_k", ctypes.c_int32),
         ("window", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
+        ("select_block", ctypes.c_int32),
     ]
 
 
@@ -82,7 +83,7 @@ lib.hs_full_attn_select.argtypes = [_KVP, _PP, _P, ctypes.c_int, _P, _P, _P, _P,
 lib.hs_sparse_attn.restype = ctypes.c_int
 lib.hs_sparse_attn.argtypes = [_KVP, _PP, _P, ctypes.c_int, _P, _P, _P, _P, ctypes.c_size_t, _P]
 lib.hs_select_from_scores.restype = ctypes.c_int
-lib.hs_select_from_scores.argtypes = [_P, _P, ctypes.POINTER(ctypes.c_int32)] + [ctypes.c_int32] * 6 + \
+lib.hs_select_from_scores.argtypes = [_P, _P, ctypes.POINTER(ctypes.c_int32)] + [ctypes.c_int32] * 7 + \
     [_P, _P, _P, ctypes.c_size_t, _P]
 lib.hs_kv_bridge.restype = ctypes.c_int
 lib.hs_kv_bridge.argtypes = [_P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_P),
@@ -199,8 +200,8 @@ class KVCache:
         return int(self.h_seq.max())
 
 
-def params(num_q_heads, q_tokens, top_k=1024, window=128, softmax_scale=0.0):
-    return hs_attn_params(num_q_heads, q_tokens, top_k, window, softmax_scale)
+def params(num_q_heads, q_tokens, top_k=1024, window=128, softmax_scale=0.0, select_block=0):
+    return hs_attn_params(num_q_heads, q_tokens, top_k, window, softmax_scale, select_block)
 
 
 def full_attn_select_workspace_size(kv, p):
@@ -220,11 +221,12 @@ def scores_stride(kv, window):
 
 
 def full_attn_select(kv, q, top_k=1024, window=128, softmax_scale=0.0, out=None, lse=None,
-                     sel_idx=None, sel_count=None, scores_out=None, ws=None, stream=None):
+                     sel_idx=None, sel_count=None, scores_out=None, ws=None, stream=None, select_block=0):
     """Full-attention layer + selection.  q [B, n_q, H, 128] (float32 or bf16).
+    select_block 64 picks whole 64-token blocks (the earlier block-level variant).
     Returns (out, lse, sel_idx, sel_count) as device tensors."""
     B, n_q, H, d = q.shape
-    p = params(H, n_q, top_k, window, softmax_scale)
+    p = params(H, n_q, top_k, window, softmax_scale, select_block)
     dev = q.device
     if out is None:
         out = torch.empty((B, n_q, H, d), dtype=torch.float32, device=dev)
@@ -257,7 +259,7 @@ def sparse_attn(kv, q, sel_idx, sel_count, top_k=1024, window=128, softmax_scale
     return out
 
 
-def select_from_scores(scores, seq_len, q_tokens, n_kv, top_k=1024, window=128, stream=None):
+def select_from_scores(scores, seq_len, q_tokens, n_kv, top_k=1024, window=128, select_block=0, stream=None):
     """Selection stage alone on given float32 scores [B, q_tokens, n_kv, S]."""
     h_seq = np.ascontiguousarray(np.asarray(seq_len, np.int32))
     B = len(h_seq)
@@ -268,7 +270,8 @@ def select_from_scores(scores, seq_len, q_tokens, n_kv, top_k=1024, window=128, 
     sel_count = torch.empty((B, q_tokens, n_kv), dtype=torch.int32, device=dev)
     ws = workspace(lib.hs_select_workspace_size(B, q_tokens, n_kv, max_len, top_k, window), dev)
     check(lib.hs_select_from_scores(_ptr(scores), _ptr(d_seq), h_seq.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-                                    B, q_tokens, n_kv, max_len, top_k, window, _ptr(sel_idx), _ptr(sel_count),
+                                    B, q_tokens, n_kv, max_len, top_k, window, select_block, _ptr(sel_idx),
+                                    _ptr(sel_count),
                                     _ptr(ws), ws.numel(), _stream(stream)))
     return sel_idx, sel_count
 

@@ -47,7 +47,7 @@ def test_exports_every_declared_symbol(hs):
 
 
 def test_version_and_strings(hs):
-    assert hs.lib.hs_abi_version() == 1
+    assert hs.lib.hs_abi_version() == 2
     assert hs.status_string(0) == "HS_OK"
     assert hs.status_string(3) == "HS_ERR_WORKSPACE_TOO_SMALL"
 
@@ -97,6 +97,7 @@ def test_full_attn_select_rejects_bad_params(hs):
     assert _call_full(hs, c, hs.params(32, 1), q=0x200004) == 1   # misaligned q
     assert _call_full(hs, c, hs.params(32, 1), q_dtype=2) == 1    # FP8 queries
     assert _call_full(hs, c, hs.params(32, 1), q=None) == 1
+    assert _call_full(hs, c, hs.params(32, 1, select_block=32)) == 2   # block size other than 64
 
 
 def test_workspace_size_and_too_small(hs):
@@ -124,9 +125,14 @@ def test_select_from_scores_rejects(hs):
     lens = np.array([10, 20], np.int32)
     lp = lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     f = hs.lib.hs_select_from_scores
-    assert f(None, 0x100000, lp, 2, 1, 1, 20, 4, 2, 0x200000, 0x300000, None, 0, None) == 1
-    assert f(0x100000, 0x100000, lp, 2, 1, 1, 15, 4, 2, 0x200000, 0x300000, None, 0, None) == 1  # L > max_len
-    assert f(0x100000, 0x100000, lp, 2, 1, 1, 20, -1, 2, 0x200000, 0x300000, None, 0, None) == 1
+    assert f(None, 0x100000, lp, 2, 1, 1, 20, 4, 2, 0, 0x200000, 0x300000, None, 0, None) == 1
+    assert f(0x100000, 0x100000, lp, 2, 1, 1, 15, 4, 2, 0, 0x200000, 0x300000, None, 0, None) == 1  # L > max_len
+    assert f(0x100000, 0x100000, lp, 2, 1, 1, 20, -1, 2, 0, 0x200000, 0x300000, None, 0, None) == 1
+    assert f(0x100000, 0x100000, lp, 2, 1, 1, 20, 4, 2, 16, 0x200000, 0x300000, 0x400000, 1 << 20, None) == 2
+    big = np.array([3_000_000], np.int32)                     # more candidates than block keys fit in LDS
+    bp = big.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    assert f(0x100000, 0x100000, bp, 1, 1, 1, 3_000_000, 1024, 128, 64, 0x200000, 0x300000, 0x400000, 1 << 40,
+             None) == 2
 
 
 def test_bridge_rejects(hs):

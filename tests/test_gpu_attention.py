@@ -194,3 +194,39 @@ def test_config3_full_size():
     assert stats["hit"] / stats["tot"] >= 0.999
     print(f"[result] config3 max|dO| {stats['err']:.3e} sparse {stats['serr']:.3e} "
           f"recall {stats['hit'] / stats['tot']:.6f}", flush=True)
+
+
+def test_block_level_variant_bf16():
+    """The earlier block-level selection through the full layer: lists equal the oracle's block
+    selection on the GPU's own scores (float32 tree order), overlap the float64 block selection,
+    and sparse layers over the block lists match the oracle."""
+    from long_context_split_amd import hysparse as hs
+    lens = [1, 300, 1153, 1217, 20000, 70001]
+    banner(f"block-level variant bf16 lens={lens}")
+    up = Uploaded(synth.decode_case(2, B=len(lens), lengths=lens))
+    kv = up.kv
+    B, n_q, H, _ = up.q_full.shape
+    S = hs.scores_stride(kv, 128)
+    sc = torch.empty((B, n_q, 1, S), dtype=torch.float32, device="cuda")
+    out, lse, idx, cnt = hs.full_attn_select(kv, up.q_full, scores_out=sc, select_block=64)
+    so = hs.sparse_attn(kv, up.q_sparse[0], idx, cnt)
+    torch.cuda.synchronize()
+    sc, idx, cnt, so = sc.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy(), so.cpu().numpy()
+    hit = tot = 0
+    for i, L in enumerate(lens):
+        w = min(128, L)
+        q, k, v = up.oracle_seq(i)
+        ref = block.full_layer(q, k, v, 1024, 128)
+        gi, gc = selection.select_blocks(np.ascontiguousarray(sc[i, 0, 0, :L - w]), L, 1024, 128, f32_tree=True)
+        assert cnt[i, 0, 0] == gc and np.array_equal(idx[i, 0, 0], gi), f"seq {i}: block lists"
+        oi, oc = selection.select_blocks(ref["s"][0, 0], L, 1024, 128)
+        assert gc == oc
+        g = set(gi[:gc - w].tolist())
+        r = set(oi[:oc - w].tolist())
+        hit += len(g & r)
+        tot += max(1, len(r))
+        qs, _, _ = up.oracle_seq(i, "sparse", 0)
+        ref_o, _ = attention.sparse_attention(qs, k, v, idx[i], cnt[i])
+        assert np.abs(so[i] - ref_o).max() <= 2e-3
+    assert hit / tot >= 0.99
+

@@ -96,3 +96,47 @@ def test_select_more_than_four_million_candidates():
     x[0, 0, 0] = rng.random(n, dtype=np.float32)
     x[1, 0, 0] = (1.0 + rng.random(n) * 0.01).astype(np.float32)
     _check(x, [L, L], 1, 1, 1024, 128)
+
+
+def _check_blocks(scores, lens, q_tokens, n_kv, top_k, window):
+    from long_context_split_amd import hysparse as hs
+    d = torch.from_numpy(scores).cuda()
+    idx, cnt = hs.select_from_scores(d, lens, q_tokens, n_kv, top_k, window, select_block=64)
+    torch.cuda.synchronize()
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    for b, L in enumerate(lens):
+        n = L - min(window, L)
+        for t in range(q_tokens):
+            for g in range(n_kv):
+                ri, rc = selection.select_blocks(scores[b, t, g, :n], L, top_k, window, f32_tree=True)
+                assert cnt[b, t, g] == rc, (b, t, g, L)
+                assert np.array_equal(idx[b, t, g], ri), (b, t, g, L)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_select_blocks_bit_exact(kind):
+    """Block-level variant: 64-token block sums in the float32 tree order, then the same ranking and
+    tie rule, bit for bit against the oracle on identical scores (partial last blocks included)."""
+    banner(f"select blocks kind={kind}")
+    lens = [1, 127, 128, 129, 1151, 1152, 1153, 1217, 2000, 5000, 70001]
+    S = max(lens) - 128
+    rng = np.random.default_rng(200 + KINDS.index(kind))
+    scores = np.zeros((len(lens), 1, 1, S), np.float32)
+    for b, L in enumerate(lens):
+        n = L - min(128, L)
+        scores[b, 0, 0, :n] = _pattern(kind, n, rng)
+    _check_blocks(scores, lens, 1, 1, 1024, 128)
+
+
+def test_select_blocks_budgets_and_long_list():
+    banner("select blocks budgets, q_tokens=2, n_kv=2, L=1048576")
+    rng = np.random.default_rng(12)
+    lens = [3000, 777]
+    full = (rng.integers(0, 9, (2, 2, 2, max(lens))) / 8).astype(np.float32)
+    # the score tensor's last dimension is max_len - window
+    _check_blocks(np.ascontiguousarray(full[..., :max(lens) - 16]), lens, 2, 2, 200, 16)   # 3 blocks, ties
+    _check_blocks(np.ascontiguousarray(full[..., :max(lens) - 4]), lens, 2, 2, 40, 4)      # < one block
+    L = 1 << 20
+    x = (rng.random(L - 128) * 1e-4).astype(np.float32)
+    x[rng.choice(L - 128, 300, replace=False)] = np.float32(5e-3)
+    _check_blocks(x.reshape(1, 1, 1, -1), [L], 1, 1, 1024, 128)
