@@ -215,7 +215,7 @@ __global__ __launch_bounds__(64 * NWR * NWT) void attn_partial_kernel(AttnArgs a
       lsum *= alpha;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        p[r] = exp2f(l2[r] - msub);
+        p[r] = exp2_fast(l2[r] - msub);
         lsum += p[r];
         if (FP8) p[r] *= vsc[tl * 32 + crow(lane, r)];            // v scale folded into P
       }
@@ -414,7 +414,7 @@ __global__ __launch_bounds__(64 * NWR * NWT) void attn_scores_kernel(ScoreArgs a
       const float f = a.scale_log2 * (FP8 ? ksc[tk] : 1.f);
       float p[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) p[r] = exp2f(s[r] * f - lse2[r]);
+      for (int r = 0; r < 16; ++r) p[r] = exp2_fast(s[r] * f - lse2[r]);
       if (tpw == 1) {
         float acc = 0.f;
 #pragma unroll

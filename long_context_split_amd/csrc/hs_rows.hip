@@ -205,7 +205,7 @@ __global__ __launch_bounds__(64 * NRG) void attn_rows_kernel(AttnArgs a) {
       float p[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        p[r] = exp2f(x[r] - m);
+        p[r] = exp2_fast(x[r] - m);
         lsum += p[r];
         if (FP8) p[r] *= vs[r];                                     // V scale folded into P
       }
@@ -377,7 +377,7 @@ __global__ __launch_bounds__(64 * NRG) void attn_rows_scores_kernel(ScoreArgs a)
       for (int q4 = 0; q4 < 4; ++q4) {
         float v = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v += exp2f(s[4 * q4 + i] * f - lse2[4 * q4 + i]);
+        for (int i = 0; i < 4; ++i) v += exp2_fast(s[4 * q4 + i] * f - lse2[4 * q4 + i]);
         blk[q4] = v + __shfl_xor(v, 32);
       }
       if (lane < 32) {

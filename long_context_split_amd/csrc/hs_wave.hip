@@ -213,7 +213,7 @@ __global__ __launch_bounds__(64 * NW) void attn_wave_kernel(AttnArgs a) {
     lsum *= alpha;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      p[r] = exp2f(l2[r] - msub);
+      p[r] = exp2_fast(l2[r] - msub);
       lsum += p[r];
       if (FP8) p[r] *= wvs[crow(lane, r)];
     }
@@ -424,7 +424,7 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
       const float f = a.scale_log2 * (FP8 ? ksc[wave][32 * half + (lane & 31)] : 1.f);
       float p[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) p[r] = exp2f(s[r] * f - lse2[r]);
+      for (int r = 0; r < 16; ++r) p[r] = exp2_fast(s[r] * f - lse2[r]);
       const int pos = c0 + tile * TT + 32 * half + (lane & 31);
       float tv[NQ];
       if (tpw == 1) {
