@@ -188,9 +188,27 @@ hs_status plan_full(const hs_kv_cache* kv, const hs_attn_params* p, hs_dtype q_d
   int chunk = env_int("HS_SPLIT_TOKENS", 0);
   if (chunk <= 0) {
     if (pl.wave) {
-      // about 512 workgroups (2 per CU-slot round), 1024..32768 tokens each
-      const int64_t per = (ci.total + 511) / 512;
-      chunk = (int)std::min<int64_t>(32768, std::max<int64_t>(1024, per));
+      // Whole rounds of workgroups (one 8-wave workgroup per CU at a time): the smallest chunk,
+      // a multiple of 256 tokens, whose workgroup count fills r rounds of 256 for the smallest r
+      // that keeps chunks <= 32768 (>= 1024).  A last round of only a few workgroups leaves HBM
+      // under-used; ragged lengths make equal-size chunks land there unless the count is planned.
+      auto wg_count = [&](int64_t c) {
+        int64_t n = 0;
+        for (int b = 0; b < ci.B; ++b) n += (kv->h_seq_len[b] + c - 1) / c;
+        return n;
+      };
+      const int64_t cmax = (int64_t)align_up((size_t)ci.maxL, 256);
+      int64_t c = 32768;
+      for (int64_t r = 1; r < 1 << 20; ++r) {
+        if (wg_count(cmax) > 256 * r) continue;                   // more sequences than slots
+        int64_t lo = 1, hi = cmax / 256;                          // in units of 256 tokens
+        while (lo < hi) {
+          const int64_t mid = (lo + hi) / 2;
+          if (wg_count(mid * 256) <= 256 * r) hi = mid; else lo = mid + 1;
+        }
+        if (lo * 256 <= 32768) { c = lo * 256; break; }
+      }
+      chunk = (int)std::max<int64_t>(1024, c);
     } else if (pl.rows) {
       // about 256 workgroups (one per CU: compute-bound, and few partials to merge), >= one super-tile
       const int64_t per = (ci.total * zb + 255) / 256;
@@ -413,6 +431,21 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
     a.zero_words = hs::SELECT_ZERO_WORDS;
     a.zero_lists = n_sel_lists;
   }
+  // items of the one-dimensional grids: chunks with work per list (lists in order)
+  // (and the per-list count when it is the same for every list, which spares the kernel the search)
+  auto count_items = [&](int chunk, int sub, int min_items, int& uniform) {
+    int64_t n = 0;
+    uniform = -1;
+    for (int b = 0; b < ci.B; ++b) {
+      const int L = kv->h_seq_len[b];
+      const int c = std::max(min_items, (L - std::min(sub, L) + chunk - 1) / chunk);
+      uniform = uniform == -1 || uniform == c ? c : 0;
+      n += (int64_t)ci.n_kv * c;
+    }
+    if (uniform < 0 || env_int("HS_GRID_SEARCH", 0)) uniform = 0;
+    return (int)n;
+  };
+  a.n_items = count_items(pl.chunk, 0, 1, a.uniform_items);
   hipError_t e;
   if (pl.wave)
     e = timed("attn_wave_dense", s, [&] { return hs::launch_attn_wave(a, kvt, false, s); });
@@ -452,7 +485,9 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
         sa.part_acc = a.part_acc; sa.part_ml = a.part_ml; sa.dchunk = pl.chunk; sa.dmax_chunks = pl.max_chunks;
         sa.out = out; sa.lse = lse;
       }
-      if ((e = timed("scores_wave", s, [&] { return hs::launch_scores_wave(sa, kvt, s); })) != hipSuccess)
+      sa.n_items = count_items(pl.chunk_s, p->window, fold_merge ? 1 : 0, sa.uniform_items);
+      if (sa.n_items > 0 &&
+          (e = timed("scores_wave", s, [&] { return hs::launch_scores_wave(sa, kvt, s); })) != hipSuccess)
         return hip_fail(e, "selection scores");
     } else if ((e = timed("attn_scores", s, [&] { return hs::launch_attn_scores(sa, kvt, pl.ct, pl.nwr_s, s); })) !=
                hipSuccess) {

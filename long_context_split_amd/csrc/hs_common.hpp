@@ -102,6 +102,52 @@ __device__ __forceinline__ void zero_words_grid(uint32_t* ptr, int64_t stride, i
     ptr[(i / words) * stride + (i % words)] = 0u;
 }
 
+// Dense one-dimensional grids over ragged lists.  List l (sequence l / n_kv) owns
+// max(min_items, ceil((L_b - min(sub, L_b)) / chunk)) consecutive items, lists in order, so a
+// launch has exactly the items that have work and the hardware's round-robin spreads them evenly
+// over the XCDs (a two-dimensional grid with early-exit blocks can leave one XCD a second round).
+// Returns (list, index within the list) of `item`, or list = -1 past the last item.  uniform > 0:
+// every list owns exactly `uniform` items (plain division, no loads).  Otherwise every thread of
+// the workgroup must call it (it ends with a barrier).
+__device__ inline void grid_item(const int32_t* seq_len, int n_kv, int n_lists, int chunk, int sub, int min_items,
+                                 int uniform, int item, int& list, int& idx) {
+  if (uniform > 0) {
+    list = item / uniform < n_lists ? item / uniform : -1;
+    idx = item % uniform;
+    return;
+  }
+  __shared__ int s_li[2];
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    if (lane == 0) s_li[0] = -1;
+    int base = 0;
+    for (int l0 = 0; l0 < n_lists; l0 += 64) {
+      const int l = l0 + lane;
+      int cnt = 0;
+      if (l < n_lists) {
+        const int L = seq_len[l / n_kv];
+        cnt = max(min_items, (L - min(sub, L) + chunk - 1) / chunk);
+      }
+      int incl = cnt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      const int tot = __shfl(incl, 63);
+      if (item < base + tot) {                                     // uniform over the wave
+        const unsigned long long m = __ballot(item < base + incl);
+        if (lane == __ffsll((long long)m) - 1) { s_li[0] = l; s_li[1] = item - (base + incl - cnt); }
+        break;
+      }
+      base += tot;
+    }
+  }
+  __syncthreads();
+  list = s_li[0];
+  idx = s_li[1];
+}
+
 // Split-K partials of one attention row: chunk c holds (m_c, l_c) at ml[c * mstride] (running max in
 // log2 units, sum of 2^(s - m_c)) and acc_c = sum 2^(s - m_c) v at acc[c * astride].
 

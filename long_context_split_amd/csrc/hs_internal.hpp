@@ -34,6 +34,8 @@ struct AttnArgs {
   float* out;            // [B, n_q, H, 128]
   float* lse;            // nullable, natural log
   float* lse2;           // nullable, log2 units
+  int n_items;           // attn_wave dense: one-dimensional grid of (list, chunk) items (grid_item)
+  int uniform_items;     //   items per list when every list has the same number, else 0
   uint32_t* zero_ptr;    // attn_wave: words cleared by the grid (nullable):
   int64_t zero_stride;   //   zero_lists runs of zero_words words, zero_stride apart
   int zero_words, zero_lists;
@@ -64,6 +66,8 @@ struct ScoreArgs {
   const float* lse2;     // [B, n_q, H]
   float* scores;         // [B, n_q, n_kv, s_stride]
   int64_t s_stride;
+  int n_items;           // scores_wave: one-dimensional grid of (list, chunk) items (grid_item)
+  int uniform_items;     //   items per list when every list has the same number, else 0
   uint32_t* hist;        // scores_wave: first-digit histograms of the selection (nullable),
   int64_t hist_stride;   //   2048 words per list, hist_stride words apart
   // scores_wave, optional: the full layer's chunk partials (as attn_wave writes them); when set,

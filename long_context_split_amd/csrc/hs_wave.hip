@@ -58,7 +58,14 @@ __global__ __launch_bounds__(64 * NW) void attn_wave_kernel(AttnArgs a) {
 
   zero_hook(a);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int list = blockIdx.y, chunk = blockIdx.x;
+  int list, chunk;
+  if (GATHER) {
+    list = blockIdx.y;
+    chunk = blockIdx.x;
+  } else {
+    grid_item(a.seq_len, a.n_kv, a.n_lists, a.chunk, 0, 1, a.uniform_items, blockIdx.x, list, chunk);
+    if (list < 0) return;
+  }
   int b, t0, g;
   if (GATHER) { g = list % a.n_kv; const int bt = list / a.n_kv; b = bt / a.n_q; t0 = bt % a.n_q; }
   else { g = list % a.n_kv; b = list / a.n_kv; t0 = 0; }
@@ -305,12 +312,15 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
 
   __shared__ float s_lse2[32];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int list = blockIdx.y;
+  int list, cidx;                                                // lists own max(fold, ceil(ncand / chunk)) items
+  grid_item(a.seq_len, a.n_kv, a.n_lists, a.chunk, a.window, a.part_ml ? 1 : 0, a.uniform_items, blockIdx.x, list,
+            cidx);
+  if (list < 0) return;
   const int g = list % a.n_kv, b = list / a.n_kv;
   const int Lb = a.seq_len[b];
   const int w = min(a.window, Lb);
   const int ncand = Lb - w;
-  const int c0 = blockIdx.x * a.chunk;
+  const int c0 = cidx * a.chunk;
   const int c1 = min(ncand, c0 + a.chunk);
   const int64_t rs = a.row_start[b];
   const char* kbase = (const char*)a.k + ((size_t)rs * a.n_kv + g) * SB;
@@ -341,13 +351,13 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
     // from the chunk partials; row r's output is merged by workgroup r % nwg of the list's nwg >= 1.
     const int nchd = (Lb + a.dchunk - 1) / a.dchunk;
     const int nwg = max(1, (ncand + a.chunk - 1) / a.chunk);
-    if ((int)blockIdx.x >= nwg) return;
+    if (cidx >= nwg) return;
     const size_t first = (size_t)list * a.dmax_chunks * a.R;
     for (int r = wave; r < a.R; r += NW) {
       const float* ml = a.part_ml + (first + r) * 2;
       const float l2 = merged_lse2(ml, (size_t)a.R * 2, nchd, lane);
       if (lane == 0) s_lse2[r] = l2;
-      if (r % nwg != (int)blockIdx.x) continue;
+      if (r % nwg != cidx) continue;
       const float2 o = l2 == -INFINITY ? make_float2(0.f, 0.f)
                                        : merged_o(ml, (size_t)a.R * 2, a.part_acc + (first + r) * D, (size_t)a.R * D,
                                                   0, nchd, 1, l2, lane);
@@ -472,7 +482,7 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
 template <int KVT, bool GATHER>
 static hipError_t launch_wave_t(const AttnArgs& a, hipStream_t st) {
   constexpr int NW = 8;
-  dim3 grid(a.max_chunks, a.n_lists, 1);
+  dim3 grid = GATHER ? dim3(a.max_chunks, a.n_lists, 1) : dim3(a.n_items, 1, 1);
   hipLaunchKernelGGL((attn_wave_kernel<KVT, NW, GATHER>), grid, dim3(64 * NW), 0, st, a);
   return hipGetLastError();
 }
@@ -487,7 +497,7 @@ hipError_t launch_attn_wave(const AttnArgs& a, int kvt, bool gather, hipStream_t
 template <int KVT, int NQ>
 static void launch_scores_wave_t(const ScoreArgs& a, hipStream_t st) {
   constexpr int NW = NQ == 1 ? 8 : 6;                            // LDS: NW x 17 KB tiles + NQ x 8 KB histograms
-  dim3 grid(a.part_ml ? std::max(a.max_chunks, 1) : a.max_chunks, a.n_lists, 1);
+  dim3 grid(a.n_items, 1, 1);
   hipLaunchKernelGGL((scores_wave_kernel<KVT, NW, NQ>), grid, dim3(64 * NW), 0, st, a);
 }
 
