@@ -12,7 +12,12 @@
 // Workgroup tile: 128 tokens x 256 columns (one target: K's 128 columns, then
 // V's), K-stage 64, 4 waves each owning 64 rows x 128 columns = one head block,
 // so a row's amax is reduced inside one wave.  MFMA v_mfma_f32_32x32x16_bf16,
-// operands from LDS (A rows of X; B as 16-bit transposed reads of W).
+// operands from LDS as 16-byte reads: A = rows of X, B = rows of W^T.  W is
+// stored transposed ([column][k]) at stage time: each thread loads the same
+// 8-column piece of two adjacent k rows and writes 32-bit (k, k+1) pairs; the
+// 16-byte k-quads of every 8-column group are XOR-swizzled by the group index,
+// which spreads both the transposing writes and the operand reads over the LDS
+// banks.
 
 #include "hs_common.hpp"
 #include "hs_internal.hpp"
@@ -22,14 +27,17 @@ namespace hs {
 namespace {
 constexpr int BM = 128, BN = 256, BK = 64, NT = 256;
 constexpr int AROW = BK * 2 + 16;               // 144 B per X row in LDS
-constexpr int BROW = BN * 2 + 16;               // 528 B per k row of W in LDS
-constexpr int STAGE = BM * AROW + BK * BROW;    // 52224 B
+constexpr int BROW = BK * 2 + 16;               // 144 B per column of W^T in LDS
+constexpr int STAGE = BM * AROW + BN * BROW;    // 55296 B
 constexpr int EPI = 4 * 64 * 128 * 2;           // per-wave 64 x 128 bf16 staging
 constexpr int SMEM = STAGE > EPI ? STAGE : EPI;
 constexpr int APT = BM * BK * 2 / 16 / NT;      // X pieces per thread per stage (4)
 constexpr int BPT = BK * BN * 2 / 16 / NT;      // W pieces per thread per stage (8)
 
 __device__ __forceinline__ int crow(int lane, int r) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// byte offset of k-quad qd (8 k values) of W^T column n: quads XOR-swizzled per 8-column group
+__device__ __forceinline__ int wt_off(int n, int qd) { return n * BROW + 16 * (qd ^ ((n >> 3) & 7)); }
 }  // namespace
 
 __global__ __launch_bounds__(NT, 2) void bridge_kernel(BridgeArgs a) {
@@ -53,9 +61,9 @@ __global__ __launch_bounds__(NT, 2) void bridge_kernel(BridgeArgs a) {
       ra[i] = gr < a.T ? *(const u32x4*)(a.x + gr * Dm + k0 + c * 8) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int i = 0; i < BPT; ++i) {
-      const int p = tid + NT * i, kr = p >> 5, np = p & 31;
-      const uint16_t* src = (np < 16 ? wk : wv) + (int64_t)(k0 + kr) * D + (np & 15) * 8;
+    for (int i = 0; i < BPT; ++i) {                               // pair i/2: k rows 2 kp, 2 kp + 1
+      const int q = tid + NT * (i >> 1), kp = q >> 5, np = q & 31;
+      const uint16_t* src = (np < 16 ? wk : wv) + (int64_t)(k0 + 2 * kp + (i & 1)) * D + (np & 15) * 8;
       rb[i] = *(const u32x4*)src;
     }
   };
@@ -66,9 +74,15 @@ __global__ __launch_bounds__(NT, 2) void bridge_kernel(BridgeArgs a) {
       *(u32x4*)(As + (p >> 3) * AROW + (p & 7) * 16) = ra[i];
     }
 #pragma unroll
-    for (int i = 0; i < BPT; ++i) {
-      const int p = tid + NT * i;
-      *(u32x4*)(Bs + (p >> 5) * BROW + (p & 31) * 16) = rb[i];
+    for (int jp = 0; jp < BPT / 2; ++jp) {                        // W^T: word (k, k + 1) of column n
+      const int q = tid + NT * jp, kp = q >> 5, np = q & 31;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t a0 = rb[2 * jp][e >> 1], a1 = rb[2 * jp + 1][e >> 1];
+        const uint32_t word = (e & 1) ? ((a0 >> 16) | (a1 & 0xFFFF0000u)) : ((a0 & 0xFFFFu) | (a1 << 16));
+        const int n = 8 * np + e;
+        *(uint32_t*)(Bs + wt_off(n, kp >> 2) + 4 * (kp & 3)) = word;
+      }
     }
   };
 
@@ -86,9 +100,8 @@ __global__ __launch_bounds__(NT, 2) void bridge_kernel(BridgeArgs a) {
         av[i] = *(const s16x8*)(As + (64 * wm + 32 * i + (lane & 31)) * AROW + (16 * s + 8 * (lane >> 5)) * 2);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const char* bp = Bs + (16 * s + 8 * (lane >> 5)) * BROW + (128 * wn + 32 * j + (lane & 31)) * 2;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) bv[j][e] = *(const short*)(bp + e * BROW);
+        const int n = 128 * wn + 32 * j + (lane & 31);
+        bv[j] = *(const s16x8*)(Bs + wt_off(n, 2 * s + (lane >> 5)));
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
