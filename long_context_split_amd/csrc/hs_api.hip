@@ -248,7 +248,7 @@ hs_status plan_full(const hs_kv_cache* kv, const hs_attn_params* p, hs_dtype q_d
 }
 
 struct SparsePlan {
-  int wave;  // 1: attn_wave (G <= 32, bf16/FP8 cache); several chunks are combined by attn_merge
+  int gather;  // 1: attn_gather (bf16 Q, bf16/FP8 cache); several chunks are combined by attn_merge
   int ct, nwr, G, n_lists, chunk, max_chunks, cap;
   size_t off_acc, off_ml, total;
 };
@@ -260,14 +260,21 @@ void plan_sparse(const hs_kv_cache* kv, const hs_attn_params* p, hs_dtype q_dtyp
   pl.nwr = pl.ct == hs::CT_F32 ? (pl.G <= 32 ? 1 : 4) : hs::rows_per_wave_group(pl.G);
   pl.n_lists = ci.B * p->q_tokens * ci.n_kv;
   pl.cap = p->top_k + p->window;
-  pl.wave = pl.ct == hs::CT_BF16 && pl.G <= 32;
-  const int tt = pl.wave ? 32 : hs::partial_tile_tokens(pl.nwr);    // attn_wave: 32-row wave tiles
+  pl.gather = pl.ct == hs::CT_BF16;
+  const int tt = pl.gather ? 32 : hs::partial_tile_tokens(pl.nwr);  // attn_gather: 32-row wave tiles
   const int tiles = (pl.cap + tt - 1) / tt;
   int per_list = std::max(1, std::min(tiles, (512 + pl.n_lists - 1) / pl.n_lists));
-  // attn_wave: 256-row chunks (5 workgroups per 1152-row list) and a merge launch beat one workgroup
-  // per list (the single-chunk direct form) on 32 lists; HS_SPARSE_CHUNK overrides (>= cap: direct)
+  // attn_gather: about one workgroup per CU (256), in chunks of at least 64 rows (a multiple of the
+  // 32-row wave tile): the layer is latency-bound, so spreading a list over more CUs shortens it
+  // until the merge's extra partials cost more than they save.  HS_SPARSE_CHUNK overrides (>= cap:
+  // one workgroup per list, no merge).
   int chunk = env_int("HS_SPARSE_CHUNK", 0);
-  if (chunk <= 0) chunk = pl.wave ? 256 : ((tiles + per_list - 1) / per_list) * tt;
+  if (chunk <= 0 && pl.gather) {
+    const int units = pl.n_lists * ((pl.G + 31) / 32);
+    const int per = std::max(1, 256 / units);
+    chunk = std::max(64, (int)align_up((size_t)((pl.cap + per - 1) / per), 32));
+  }
+  if (chunk <= 0) chunk = ((tiles + per_list - 1) / per_list) * tt;
   pl.chunk = std::min((int)align_up((size_t)chunk, (size_t)tt), 1152);
   pl.max_chunks = (pl.cap + pl.chunk - 1) / pl.chunk;
   size_t off = 0;
@@ -448,7 +455,7 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
   a.n_items = count_items(pl.chunk, 0, 1, a.uniform_items);
   hipError_t e;
   if (pl.wave)
-    e = timed("attn_wave_dense", s, [&] { return hs::launch_attn_wave(a, kvt, false, s); });
+    e = timed("attn_wave_dense", s, [&] { return hs::launch_attn_wave(a, kvt, s); });
   else if (pl.rows)
     e = timed("attn_rows_dense", s, [&] { return hs::launch_attn_rows(a, kvt, pl.nrg, s); });
   else
@@ -540,14 +547,14 @@ hs_status hs_sparse_attn(const hs_kv_cache* kv, const hs_attn_params* p, const v
   a.scale_log2 = scale_log2(p);
   a.sel_idx = sel_idx; a.sel_count = sel_count; a.sel_cap = pl.cap;
   a.part_acc = (float*)(ws + pl.off_acc); a.part_ml = (float*)(ws + pl.off_ml);
-  if (pl.wave) {
+  if (pl.gather) {
     a.direct = pl.max_chunks == 1; a.out = out; a.lse = nullptr; a.lse2 = nullptr;
-    hipError_t e = timed("attn_wave_gather", s, [&] { return hs::launch_attn_wave(a, kv_type(kv->dtype), true, s); });
+    hipError_t e = timed("attn_gather", s, [&] { return hs::launch_attn_gather(a, kv_type(kv->dtype), s); });
     if (e != hipSuccess) return hip_fail(e, "sparse attention");
     if (a.direct) return HS_OK;
   }
   hipError_t e = hipSuccess;
-  if (!pl.wave) {
+  if (!pl.gather) {
     e = timed("attn_partial_gather", s, [&] { return hs::launch_attn_partial(a, kv_type(kv->dtype), pl.ct, pl.nwr, true, s); });
     if (e != hipSuccess) return hip_fail(e, "sparse attention");
   }

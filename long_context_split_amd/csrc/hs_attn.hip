@@ -111,7 +111,8 @@ __global__ __launch_bounds__(64 * NWR * NWT) void attn_partial_kernel(AttnArgs a
   constexpr bool SPLIT = (CT == CT_BF16) && (KVT != KV_FP8);
   constexpr int MAXG = 1152;                                      // gather chunk limit
   constexpr int TILES = 2 * TT * ROWB;
-  constexpr int MERGE = NWT > 1 ? NWR * NWT * 32 * (D * 4 + 8) : 0;
+  constexpr int DP = D + 4;                                      // merge row pitch: 32 rows on distinct banks
+  constexpr int MERGE = NWT > 1 ? NWR * NWT * 32 * (DP * 4 + 8) : 0;
   __shared__ __align__(16) char smem[TILES > MERGE ? TILES : MERGE];
   char* const kt = smem;
   char* const vt = smem + TT * ROWB;
@@ -245,10 +246,10 @@ __global__ __launch_bounds__(64 * NWR * NWT) void attn_partial_kernel(AttnArgs a
     }
   } else {
     // merge the NWT token lanes of each row group through LDS (tile buffers are free now)
-    float* accb = (float*)smem;                                   // [gr][tl][32 rows][128]
-    float* mlb = accb + NWR * NWT * 32 * D;                       // [gr][tl][32][2]
+    float* accb = (float*)smem;                                   // [gr][tl][32 rows][DP]
+    float* mlb = accb + NWR * NWT * 32 * DP;                      // [gr][tl][32][2]
     {
-      float* mine = accb + ((gr * NWT + tl) * 32 + (lane & 31)) * D;
+      float* mine = accb + ((gr * NWT + tl) * 32 + (lane & 31)) * DP;
 #pragma unroll
       for (int mt4 = 0; mt4 < 4; ++mt4)
 #pragma unroll
@@ -284,7 +285,7 @@ __global__ __launch_bounds__(64 * NWR * NWT) void attn_partial_kernel(AttnArgs a
       for (int e = 0; e < PER; e += 4) {
         f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < NWT; ++j) o += w[j] * *(const f32x4*)(accb + ((g2 * NWT + j) * 32 + lr) * D + d0 + e);
+        for (int j = 0; j < NWT; ++j) o += w[j] * *(const f32x4*)(accb + ((g2 * NWT + j) * 32 + lr) * DP + d0 + e);
         *(f32x4*)(pa + e) = o;
       }
       if (d0 == 0) *(float2*)(a.part_ml + (item * a.R + grow) * 2) = make_float2(mx, ls);
@@ -294,37 +295,47 @@ __global__ __launch_bounds__(64 * NWR * NWT) void attn_partial_kernel(AttnArgs a
 
 // ---------------------------------------------------------------- merge
 
-// One thread per (row, d): combines the chunks of a list in increasing order.
+// Combines the chunks of a list for each row.  ROWW (few chunks, e.g. a sparse layer): one wave per
+// (row, list), all chunks in one online pass; otherwise one workgroup per (row, list) whose wave w
+// combines chunks w, w + 4, ..., then wave 0 combines the four parts in a fixed order.  The first
+// partial loads do not wait for the list's count (merge_part_wave).
+template <bool ROWW>
 __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
-  // one workgroup per (row, list): wave w combines chunks w, w + 4, ... in one online pass, then
-  // wave 0 combines the four (m, l, o) in a fixed order
-  __shared__ float2 po[4][64];
+  __shared__ float2 po[ROWW ? 1 : 4][64];
   __shared__ float pm[4], pl[4];
-  const int list = blockIdx.y, row = blockIdx.x;
+  const int list = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = ROWW ? blockIdx.x * 4 + wave : blockIdx.x;
+  if (ROWW && row >= a.R) return;
   int b, t, g;
   if (a.gather) { g = list % a.n_kv; const int bt = list / a.n_kv; b = bt / a.n_q; t = bt % a.n_q; }
   else { g = list % a.n_kv; b = list / a.n_kv; t = row / a.G; }
   const int hh = row % a.G;
   const int ntok = a.gather ? min(max(a.sel_count[list], 0), a.sel_cap) : a.seq_len[b];
-  const int nch = (ntok + a.chunk - 1) / a.chunk;
+  const int nch = min((ntok + a.chunk - 1) / a.chunk, a.max_chunks);
   const size_t first = (size_t)list * a.max_chunks * a.R + row;
-  const MergePart r = merge_part_wave(a.part_ml + first * 2, (size_t)a.R * 2, a.part_acc + first * D,
-                                      (size_t)a.R * D, wave, nch, 4, lane);
-  po[wave][lane] = r.o;
-  if (lane == 0) { pm[wave] = r.m; pl[wave] = r.l; }
-  __syncthreads();
-  if (wave) return;
-  const float mx = fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3]));
-  const float msub = mx == -INFINITY ? 0.f : mx;
-  float ls = 0.f;
-  float2 o = make_float2(0.f, 0.f);
+  const MergePart r = merge_part_wave(a.part_ml + first * 2, (size_t)a.R * 2, a.part_acc + first * D, (size_t)a.R * D,
+                                      ROWW ? 0 : wave, nch, a.max_chunks, ROWW ? 1 : 4, lane);
+  float mx, ls;
+  float2 o;
+  if constexpr (ROWW) {
+    mx = r.m; ls = r.l; o = r.o;
+  } else {
+    po[wave][lane] = r.o;
+    if (lane == 0) { pm[wave] = r.m; pl[wave] = r.l; }
+    __syncthreads();
+    if (wave) return;
+    mx = fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3]));
+    const float msub = mx == -INFINITY ? 0.f : mx;
+    ls = 0.f;
+    o = make_float2(0.f, 0.f);
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float wt = exp2f(pm[w] - msub);
-    ls += wt * pl[w];
-    o.x += wt * po[w][lane].x;
-    o.y += wt * po[w][lane].y;
+    for (int w = 0; w < 4; ++w) {
+      const float wt = exp2f(pm[w] - msub);
+      ls += wt * pl[w];
+      o.x += wt * po[w][lane].x;
+      o.y += wt * po[w][lane].y;
+    }
   }
   const float inv = ls > 0.f ? 1.f / ls : 0.f;
   const size_t orow = ((size_t)b * a.n_q + t) * a.H + (size_t)g * a.G + hh;
@@ -506,8 +517,13 @@ hipError_t launch_attn_partial(const AttnArgs& a, int kvt, int ct, int nwr, bool
 }
 
 hipError_t launch_attn_merge(const MergeArgs& m, hipStream_t st) {
-  dim3 grid(m.R, m.n_lists);
-  hipLaunchKernelGGL(attn_merge_kernel, grid, dim3(256), 0, st, m);
+  if (m.max_chunks <= 16) {
+    dim3 grid((m.R + 3) / 4, m.n_lists);
+    hipLaunchKernelGGL(attn_merge_kernel<true>, grid, dim3(256), 0, st, m);
+  } else {
+    dim3 grid(m.R, m.n_lists);
+    hipLaunchKernelGGL(attn_merge_kernel<false>, grid, dim3(256), 0, st, m);
+  }
   return hipGetLastError();
 }
 

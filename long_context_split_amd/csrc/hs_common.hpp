@@ -79,6 +79,14 @@ __device__ __forceinline__ uint32_t f32_key(float x) {
 // not need (five more instructions per element).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Orders a wave's own LDS writes before its later reads (and reads before later writes) of the
+// same wave-private buffer.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -177,39 +185,44 @@ __device__ inline float merged_lse2(const float* ml, size_t mstride, int nch, in
 // One wave's share of a row's partials, chunks c = c_first, c_first + step, ... < nch, combined in a
 // single online pass (8 chunks in flight): running max m, l and o relative to it (lanes holding
 // d = 2 lane, 2 lane + 1).  m = -inf if the wave had no chunk.  m and l are the same on every lane.
+// Addresses are clamped to the first nld >= nch chunks rather than to nch, so the first loads need
+// not wait for nch (a count read from memory) once c_first < nld is known: chunks past nch are
+// replaced by empty parts whatever their memory holds.
 struct MergePart {
   float m, l;
   float2 o;
 };
 
 __device__ inline MergePart merge_part_wave(const float* ml, size_t mstride, const float* acc, size_t astride,
-                                            int c_first, int nch, int step, int lane) {
+                                            int c_first, int nch, int nld, int step, int lane) {
   MergePart r{-INFINITY, 0.f, make_float2(0.f, 0.f)};
-  for (int c0 = c_first; c0 < nch; c0 += 8 * step) {
+  for (int c0 = c_first; c0 < nld; c0 += 8 * step) {
     float2 q[8], x[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int c = c0 + u * step, cc = min(c, nch - 1);
+      const int c = c0 + u * step, cc = min(c, nld - 1);
       q[u] = *(const float2*)(ml + (size_t)cc * mstride);
       x[u] = *(const float2*)(acc + (size_t)cc * astride + 2 * lane);
-      if (c >= nch) q[u] = make_float2(-INFINITY, 0.f);
+      if (c >= nch) { q[u] = make_float2(-INFINITY, 0.f); x[u] = make_float2(0.f, 0.f); }
     }
     float nm = r.m;
 #pragma unroll
     for (int u = 0; u < 8; ++u) nm = fmaxf(nm, q[u].x);
-    if (nm == -INFINITY) continue;
-    const float al = exp2f(r.m - nm);
-    r.l *= al;
-    r.o.x *= al;
-    r.o.y *= al;
+    if (nm != -INFINITY) {
+      const float al = exp2f(r.m - nm);
+      r.l *= al;
+      r.o.x *= al;
+      r.o.y *= al;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float w = exp2f(q[u].x - nm);
-      r.l += w * q[u].y;
-      r.o.x += w * x[u].x;
-      r.o.y += w * x[u].y;
+      for (int u = 0; u < 8; ++u) {
+        const float w = exp2f(q[u].x - nm);
+        r.l += w * q[u].y;
+        r.o.x += w * x[u].x;
+        r.o.y += w * x[u].y;
+      }
+      r.m = nm;
     }
-    r.m = nm;
+    if (c0 + 8 * step >= nch) break;
   }
   return r;
 }

@@ -135,7 +135,9 @@ int partial_tile_tokens(int nwr);
 // nwr: query-row wave groups per workgroup, as planned by the host (1, 2, 4, 8; fp32 compute: 1 or 4)
 hipError_t launch_attn_partial(const AttnArgs& a, int kvt, int ct, int nwr, bool gather, hipStream_t st);
 // attn_wave: R <= 32 query rows per list, bf16 or FP8 caches, 8 independent waves per workgroup
-hipError_t launch_attn_wave(const AttnArgs& a, int kvt, bool gather, hipStream_t st);
+hipError_t launch_attn_wave(const AttnArgs& a, int kvt, hipStream_t st);
+// sparse layer, bf16 Q with a bf16 or FP8 cache, any G (blocks of 32 heads); chunk a multiple of 32
+hipError_t launch_attn_gather(const AttnArgs& a, int kvt, hipStream_t st);
 hipError_t launch_attn_merge(const MergeArgs& m, hipStream_t st);
 // attn_rows: dense pass 1 for R > 32 query rows per list, bf16 or FP8 caches, bf16 MFMA;
 // nrg = query-row groups of 32 per workgroup (2, 4 or 8; rows beyond 32*nrg take more z blocks)

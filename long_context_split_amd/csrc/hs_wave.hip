@@ -4,12 +4,12 @@
 // Every wave streams its own 32-token tiles with no workgroup barrier in the
 // loop, so a CU keeps many independent tiles in flight from HBM.
 //
-//  attn_wave    full layer (dense, all L_b rows) or sparse layer (gather: the
-//               rows of a selection list).  ithome page "小米公开 MiMo-V3 核心架构
-//               HySparse2", section "KV Reuse": the sparse layers read the full
-//               layer's cache at the positions it selected.  A workgroup whose
-//               chunk is the whole list writes O (and LSE) itself; otherwise it
-//               writes one (m, l, acc) partial and attn_merge combines them.
+//  attn_wave    full layer, split-K pass 1 over all L_b rows (ithome page
+//               "小米公开 MiMo-V3 核心架构 HySparse2", section "KV Reuse": the full
+//               layer attends to every cached row).  A workgroup whose chunk is
+//               the whole sequence writes O (and LSE) itself; otherwise it writes
+//               one (m, l, acc) partial that the score pass or attn_merge
+//               combines.
 //  scores_wave  second pass of the full layer: s_j = sum over the heads of a
 //               group of exp(l_j - LSE) for the candidates outside the recent
 //               window (ithome page, "KV Reuse" and recent-window paragraphs),
@@ -25,12 +25,6 @@ namespace hs {
 
 namespace {
 
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Clears the words the caller asked for (the selection's histograms) with the whole grid.
 __device__ __forceinline__ void zero_hook(const AttnArgs& a) {
   zero_words_grid(a.zero_ptr, a.zero_stride, a.zero_words, a.zero_lists);
@@ -38,7 +32,7 @@ __device__ __forceinline__ void zero_hook(const AttnArgs& a) {
 
 }  // namespace
 
-template <int KVT, int NW, bool GATHER>
+template <int KVT, int NW>
 __global__ __launch_bounds__(64 * NW) void attn_wave_kernel(AttnArgs a) {
   constexpr int NT = 64 * NW;
   using M = Mma<CT_BF16>;
@@ -48,42 +42,23 @@ __global__ __launch_bounds__(64 * NW) void attn_wave_kernel(AttnArgs a) {
   constexpr int SB = (KVT == KV_BF16 ? 2 : 1) * D;               // storage bytes per row
   constexpr int PPR = SB / 16;                                   // 16-byte pieces per row
   constexpr int PPL = 32 * PPR / 64;                             // pieces per lane per tensor
-  constexpr int MAXG = 1152;
   constexpr int TILES = NW * 2 * 32 * ROWB;
-  constexpr int MERGE = NW * 32 * (D + 2) * 4;
+  constexpr int DP = D + 4;                                      // merge row pitch: 32 heads' rows on distinct banks
+  constexpr int MERGE = NW * 32 * (DP + 2) * 4;
   __shared__ __align__(16) char smem[TILES > MERGE ? TILES : MERGE];
   __shared__ __align__(16) char qs[32 * ROWB];
   __shared__ float ksc[FP8 ? NW * 32 : 1], vsc[FP8 ? NW * 32 : 1];
-  __shared__ int gidx[GATHER ? MAXG + 32 : 1];
 
   zero_hook(a);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int list, chunk;
-  if (GATHER) {
-    list = blockIdx.y;
-    chunk = blockIdx.x;
-  } else {
-    grid_item(a.seq_len, a.n_kv, a.n_lists, a.chunk, 0, 1, a.uniform_items, blockIdx.x, list, chunk);
-    if (list < 0) return;
-  }
-  int b, t0, g;
-  if (GATHER) { g = list % a.n_kv; const int bt = list / a.n_kv; b = bt / a.n_q; t0 = bt % a.n_q; }
-  else { g = list % a.n_kv; b = list / a.n_kv; t0 = 0; }
+  grid_item(a.seq_len, a.n_kv, a.n_lists, a.chunk, 0, 1, a.uniform_items, blockIdx.x, list, chunk);
+  if (list < 0) return;
+  const int g = list % a.n_kv, b = list / a.n_kv, t0 = 0;
   const int c0 = chunk * a.chunk;
-  // GATHER: the rows of this wave's first tile come straight from the index list (clamped into the
-  // list, validated below), issued before anything else so the K/V loads wait for one load only.
-  const int32_t* il = GATHER ? a.sel_idx + (size_t)list * a.sel_cap : nullptr;
-  const int cend = GATHER ? min(c0 + a.chunk, a.sel_cap) : 0;
-  int frow[GATHER ? PPL : 1], fsrow = 0;
-  if (GATHER) {
-#pragma unroll
-    for (int i = 0; i < PPL; ++i) frow[i] = il[min(c0 + wave * 32 + (lane + 64 * i) / PPR, cend - 1)];
-    if (FP8) fsrow = il[min(c0 + wave * 32 + (lane & 31), cend - 1)];
-  }
   const int Lb = a.seq_len[b];
-  const int ntok = GATHER ? min(max(a.sel_count[(size_t)list], 0), a.sel_cap) : Lb;
-  if (c0 >= ntok) return;
-  const int c1 = min(ntok, c0 + a.chunk);
+  if (c0 >= Lb) return;
+  const int c1 = min(Lb, c0 + a.chunk);
   const int64_t rs = a.row_start[b];
   const char* kbase = (const char*)a.k + ((size_t)rs * a.n_kv + g) * SB;
   const char* vbase = (const char*)a.v + ((size_t)rs * a.n_kv + g) * SB;
@@ -95,14 +70,10 @@ __global__ __launch_bounds__(64 * NW) void attn_wave_kernel(AttnArgs a) {
   float* const wks = FP8 ? ksc + wave * 32 : nullptr;
   float* const wvs = FP8 ? vsc + wave * 32 : nullptr;
 
-  // Cache row of a tile position, clamped into the list so every load stays in bounds and needs no
+  // Cache row of a tile position, clamped into the chunk so every load stays in bounds and needs no
   // branch (a branch around a load makes the compiler wait for it at the join); positions past the
-  // chunk and invalid indices are masked in the softmax instead.
-  auto tok_row = [&](int tile, int tok) -> int {
-    const int pos = min(c0 + tile * 32 + tok, c1 - 1);
-    return GATHER ? max(gidx[pos - c0], 0) : pos;
-  };
-  auto valid_row = [&](int j) -> int { return (j >= 0 && j < Lb) ? j : 0; };
+  // chunk are masked in the softmax instead.
+  auto tok_row = [&](int tile, int tok) -> int { return min(c0 + tile * 32 + tok, c1 - 1); };
   u32x4 rk[PPL], rv[PPL];
   float sk = 0.f, sv = 0.f;
   auto load_rows = [&](auto row_of, int srow) {
@@ -120,11 +91,7 @@ __global__ __launch_bounds__(64 * NW) void attn_wave_kernel(AttnArgs a) {
   auto load = [&](int tile) {
     load_rows([&](int i) { return tok_row(tile, (lane + 64 * i) / PPR); }, FP8 ? tok_row(tile, lane & 31) : 0);
   };
-  if (wave < ntiles) {                                            // first tile, before the Q barrier
-    if (GATHER) load_rows([&](int i) { return valid_row(frow[i]); }, valid_row(fsrow));
-    else load_rows([&](int i) { return min(c0 + wave * 32 + (lane + 64 * i) / PPR, c1 - 1); },
-                   min(c0 + wave * 32 + (lane & 31), c1 - 1));
-  }
+  if (wave < ntiles) load(wave);                                  // first tile, before the Q barrier
 
   // Q rows -> LDS (row r = tt*G + hh; rows >= R are zero)
   for (int p = tid; p < 32 * 16; p += NT) {
@@ -141,12 +108,6 @@ __global__ __launch_bounds__(64 * NW) void attn_wave_kernel(AttnArgs a) {
       }
     }
     *(u32x4*)(qs + r * ROWB + c * 16) = x;
-  }
-  if (GATHER) {
-    for (int i = tid; i < c1 - c0; i += NT) {
-      const int j = il[c0 + i];
-      gidx[i] = (j >= 0 && j < Lb) ? j : -1;
-    }
   }
   __syncthreads();
 
@@ -204,9 +165,7 @@ __global__ __launch_bounds__(64 * NW) void attn_wave_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int tk = crow(lane, r);
-      const int pos = c0 + tile * 32 + tk;
-      bool ok = pos < c1;
-      if (GATHER) ok = ok && gidx[pos - c0] >= 0;
+      const bool ok = c0 + tile * 32 + tk < c1;
       float x = s[r] * sl2;
       if (FP8) x *= wks[tk];
       l2[r] = ok ? x : -INFINITY;
@@ -233,10 +192,10 @@ __global__ __launch_bounds__(64 * NW) void attn_wave_kernel(AttnArgs a) {
 
   // merge the NW waves (fixed order) through LDS
   __syncthreads();
-  float* accb = (float*)smem;                                     // [wave][32 rows][128]
-  float* mlb = accb + NW * 32 * D;                                // [wave][32][2]
+  float* accb = (float*)smem;                                     // [wave][32 rows][DP]
+  float* mlb = accb + NW * 32 * DP;                               // [wave][32][2]
   {
-    float* mine = accb + (wave * 32 + (lane & 31)) * D;
+    float* mine = accb + (wave * 32 + (lane & 31)) * DP;
 #pragma unroll
     for (int mt4 = 0; mt4 < 4; ++mt4)
 #pragma unroll
@@ -266,7 +225,7 @@ __global__ __launch_bounds__(64 * NW) void attn_wave_kernel(AttnArgs a) {
     const float wj = exp2f(mlb[(j * 32 + row) * 2] - msub);
     ls += wj * mlb[(j * 32 + row) * 2 + 1];
 #pragma unroll
-    for (int e = 0; e < PER / 4; ++e) o[e] += wj * *(const f32x4*)(accb + (j * 32 + row) * D + d0 + 4 * e);
+    for (int e = 0; e < PER / 4; ++e) o[e] += wj * *(const f32x4*)(accb + (j * 32 + row) * DP + d0 + 4 * e);
   }
   const int t = t0 + (row_ok ? row / a.G : 0), hh = row_ok ? row % a.G : 0;
   const size_t orow = ((size_t)b * a.n_q + t) * a.H + (size_t)g * a.G + hh;
@@ -479,18 +438,17 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
   }
 }
 
-template <int KVT, bool GATHER>
+template <int KVT>
 static hipError_t launch_wave_t(const AttnArgs& a, hipStream_t st) {
   constexpr int NW = 8;
-  dim3 grid = GATHER ? dim3(a.max_chunks, a.n_lists, 1) : dim3(a.n_items, 1, 1);
-  hipLaunchKernelGGL((attn_wave_kernel<KVT, NW, GATHER>), grid, dim3(64 * NW), 0, st, a);
+  hipLaunchKernelGGL((attn_wave_kernel<KVT, NW>), dim3(a.n_items), dim3(64 * NW), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_wave(const AttnArgs& a, int kvt, bool gather, hipStream_t st) {
+hipError_t launch_attn_wave(const AttnArgs& a, int kvt, hipStream_t st) {
   if (a.R > 32) return hipErrorInvalidValue;
-  if (kvt == KV_BF16) return gather ? launch_wave_t<KV_BF16, true>(a, st) : launch_wave_t<KV_BF16, false>(a, st);
-  if (kvt == KV_FP8) return gather ? launch_wave_t<KV_FP8, true>(a, st) : launch_wave_t<KV_FP8, false>(a, st);
+  if (kvt == KV_BF16) return launch_wave_t<KV_BF16>(a, st);
+  if (kvt == KV_FP8) return launch_wave_t<KV_FP8>(a, st);
   return hipErrorInvalidValue;
 }
 

@@ -121,6 +121,52 @@ def test_ragged_bf16_edge_lengths(split, schunk, monkeypatch):
             assert np.abs(res["sparse"][0][i] - full).max() <= 2e-3
 
 
+@pytest.mark.parametrize("kvtype,H,schunk", [("bf16", 32, 0), ("bf16", 48, 512), ("e4m3", 64, 0), ("e4m3", 32, 1152)])
+def test_sparse_lists_with_absent_entries(kvtype, H, schunk, monkeypatch):
+    """Sparse layer on hand-made lists: ragged counts (1 row; 300 rows, ending inside a 256-row
+    chunk; the full 1152), repeated rows, and entries outside [0, L_b) inside the count, which the
+    layer treats as absent.  H=48 leaves the second block of 32 query heads half empty; chunk 512
+    gives each wave two tiles and 1152 is the single-workgroup direct form.  Oracle: the same lists
+    with the absent entries removed."""
+    from long_context_split_amd import hysparse as hs
+    if schunk:
+        monkeypatch.setenv("HS_SPARSE_CHUNK", str(schunk))
+    banner(f"sparse lists with absent entries kv={kvtype} H={H} chunk={schunk}")
+    rng = np.random.default_rng(11)
+    lens = [3000, 900, 1500]
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    tot = sum(lens)
+    kf = rng.standard_normal((tot, 1, 128)).astype(np.float32)
+    vf = rng.standard_normal((tot, 1, 128)).astype(np.float32)
+    q = synth.bf16_bits(rng.standard_normal((3, 1, H, 128)).astype(np.float32))
+    if kvtype == "bf16":
+        kf, vf = synth.bf16_bits(kf), synth.bf16_bits(vf)
+    case = dict(spec=dict(kv=kvtype, q="bf16"), lengths=np.array(lens), row_start=starts,
+                q_full=q, q_sparse=[q], k=kf, v=vf, needles=[[], [], []])
+    up = Uploaded(case)
+    cap = 1152
+    idx = np.full((3, 1, 1, cap), -1, np.int32)
+    cnt = np.array([cap, 1, 300], np.int32).reshape(3, 1, 1)
+    idx[0, 0, 0] = rng.integers(0, lens[0], cap)                     # with repeats
+    idx[0, 0, 0, [5, 40, 41, 700, 1151]] = [-1, lens[0], -7, 10 ** 6, lens[0] + 1]
+    idx[1, 0, 0, 0] = 899
+    idx[2, 0, 0, :300] = rng.permutation(lens[2])[:300]
+    idx[2, 0, 0, [0, 255, 256, 299]] = [-2, lens[2], -1, 2 ** 31 - 1]
+    out = hs.sparse_attn(up.kv, up.q_sparse[0], torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda())
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    worst = 0.0
+    for i in range(3):
+        qs, k, v = up.oracle_seq(i, "sparse", 0)
+        sel = idx[i, 0, 0, :cnt[i, 0, 0]]
+        sel = sel[(sel >= 0) & (sel < lens[i])]
+        ref, _ = attention.sparse_attention(qs, k, v, sel.reshape(1, 1, -1), np.array([[sel.size]]))
+        e = np.abs(out[i] - ref).max()
+        worst = max(worst, float(e))
+        assert e <= TOL[kvtype], f"seq {i}: max|dO| = {e}"
+    print(f"[result] absent-entry lists kv={kvtype} H={H} chunk={schunk} max|dO| {worst:.3e}", flush=True)
+
+
 def test_gqa_multi_query_tokens_bf16():
     """n_kv = 2 KV heads of 16 query heads each, 3 query tokens (no mask among them)."""
     banner("gqa n_kv=2 H=32 n_q=3 bf16")
