@@ -467,6 +467,13 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
   m.gather = 0; m.n_kv = ci.n_kv; m.H = a.H; m.G = pl.G; m.n_q = a.n_q; m.R = pl.R; m.n_lists = pl.n_lists;
   m.chunk = pl.chunk; m.max_chunks = pl.max_chunks; m.out = out; m.lse = lse; m.lse2 = lse2;
   const bool fold_merge = pl.wave && !a.direct && pl.max_chunks <= 64;   // scores_wave merges O, writes LSE
+  // candidate mode (scores_wave, one query token, equal lengths): the score pass appends the pairs
+  // that can still reach the k'-th key and the selection runs on them in one workgroup per list;
+  // dense scores only on request
+  bool equal_len = true;
+  for (int b = 1; b < ci.B; ++b) equal_len = equal_len && kv->h_seq_len[b] == kv->h_seq_len[0];
+  const bool cand_mode = pl.wave && p->q_tokens == 1 && equal_len && p->select_block == 0 &&
+                         pl.s_stride <= hs::SELECT_CAND_MAX_N && !env_int("HS_DENSE_SELECT", 0);
   if (!a.direct && !fold_merge)                                   // several chunks: merge them
     if ((e = timed("attn_merge_dense", s, [&] { return hs::launch_attn_merge(m, s); })) != hipSuccess)
       return hip_fail(e, "full attention merge");
@@ -493,6 +500,13 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
         sa.out = out; sa.lse = lse;
       }
       sa.n_items = count_items(pl.chunk_s, p->window, fold_merge ? 1 : 0, sa.uniform_items);
+      if (cand_mode) {                                            // about one workgroup per CU, each on one list
+        sa.scores = scores_out;                                   // nullable: the test hook only
+        sa.cand_off = pl.sel.cand_off;
+        sa.top_k = p->top_k;
+        sa.chunk = hs::scores_cand_chunk();
+        sa.n_items = pl.n_lists * std::max(1, 256 / pl.n_lists);
+      }
       if (sa.n_items > 0 &&
           (e = timed("scores_wave", s, [&] { return hs::launch_scores_wave(sa, kvt, s); })) != hipSuccess)
         return hip_fail(e, "selection scores");
@@ -510,6 +524,8 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
   se.chunk = pl.sel.chunk; se.max_chunks = pl.sel.max_chunks;
   if (p->select_block == 64)
     e = timed("select_blocks", s, [&] { return hs::launch_select_blocks(se, n_sel_lists, pl.s_stride, s); });
+  else if (cand_mode)
+    e = timed("select_cand", s, [&] { return hs::launch_select_cand(se, n_sel_lists, s); });
   else
     e = timed("select_topk", s, [&] { return hs::launch_select(se, n_sel_lists, fused_prefix, s); });
   if (e != hipSuccess) return hip_fail(e, "selection");

@@ -77,6 +77,14 @@ struct ScoreArgs {
   int dchunk, dmax_chunks;
   float* out;
   float* lse;            // nullable, natural log
+  // scores_wave, candidate mode (cand_off > 0; one query token, hist set, chunk =
+  // scores_cand_chunk(), n_items = workgroups, a multiple of n_lists): workgroup w keeps list
+  // w % n_lists and appends the (key, index) pairs of every score whose first digit is at or
+  // above the lowest digit the k'-th key can still have (from the list's histogram as it fills)
+  // to the list's candidate buffer (hist + cand_off words, count at SELECT_CCOUNT_WORD);
+  // `scores` may then be null (no dense scores written)
+  int64_t cand_off;
+  int top_k;
 };
 
 struct SelectArgs {
@@ -155,7 +163,14 @@ hipError_t launch_select(const SelectArgs& a, int n_lists, bool fused_prefix, hi
 hipError_t launch_select_blocks(const SelectArgs& a, int n_lists, int64_t max_cand, hipStream_t st);
 int64_t select_blocks_max_candidates();
 hipError_t launch_scores_wave(const ScoreArgs& a, int kvt, hipStream_t st);
+// candidate mode of scores_wave: tokens per item (ScoreArgs::chunk), items walked chunk-major
+int scores_cand_chunk();
 constexpr int SELECT_ZERO_WORDS = 4100;   // per-list words the selection needs cleared
+constexpr int SELECT_CCOUNT_WORD = 4096;  // per-list word: candidate pairs appended so far
+// candidate mode: the score pass appended the candidate pairs (ScoreArgs::cand_off); one workgroup
+// per list, lists of at most SELECT_CAND_MAX_N candidates (an LDS bitmap over them)
+constexpr int SELECT_CAND_MAX_N = 1 << 20;
+hipError_t launch_select_cand(const SelectArgs& a, int n_lists, hipStream_t st);
 hipError_t launch_bridge(const BridgeArgs& a, hipStream_t st);
 
 }  // namespace hs

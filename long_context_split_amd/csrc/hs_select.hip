@@ -90,12 +90,12 @@ __device__ __forceinline__ uint32_t block_scan_excl(uint32_t v, uint32_t* sh, ui
 template <int NT, int NB>
 __device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t rem, uint32_t* sh, uint32_t& digit,
                                            uint32_t& rem_out) {
-  constexpr int PER = NB / NT;
+  constexpr int PER = NB >= NT ? NB / NT : 1;                   // fewer bins than threads: one each
   const int t = threadIdx.x;
   uint32_t h[PER], sum = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    h[i] = hist[t * PER + i];
+    h[i] = t * PER + i < NB ? hist[t * PER + i] : 0u;
     sum += h[i];
   }
   uint32_t tot;
@@ -337,6 +337,132 @@ __global__ __launch_bounds__(CH_NT) void sel_write_kernel(SelectArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- candidate mode
+//
+// The score pass appended, per list, the (key, index) pairs of every score whose first digit could
+// still reach the k'-th key (all pairs of the boundary digit and above, in no particular order) and
+// built the full first-digit histogram.  Its scores are >= +0, so every key has bit 31 set and the
+// digits are bits 30..20, 19..9 and 8..0.  One workgroup per list:
+//   * first digit from the histogram; the second and third digits from the candidates in the
+//     boundary bin -> the exact k'-th key T and the number `need` of keys equal to T taken;
+//   * the selected positions are set in an LDS bitmap over the list's candidates (ties to T: a
+//     first bitmap of the tied positions gives the position of the need-th one, so the lowest
+//     indices win);
+//   * the bitmap read in order yields the ascending index list without a sort.
+constexpr int CAND_MAX_WORDS = SELECT_CAND_MAX_N / 32;    // bitmap words in LDS (128 KB)
+
+__global__ __launch_bounds__(FIN_NT) void sel_cand_select_kernel(SelectArgs a) {
+  const int list = blockIdx.x;
+  const ListInfo li = list_info(a, list);
+  int32_t* out = a.sel_idx + (size_t)list * a.cap;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < li.w; i += FIN_NT) out[li.kk + i] = li.n + i;   // window rows L-W' .. L-1
+  for (int i = li.kk + li.w + tid; i < a.cap; i += FIN_NT) out[i] = -1;
+  if (tid == 0) a.sel_count[list] = li.kk + li.w;
+  if (li.kk == 0) return;
+  if (li.kk >= li.n) {                                            // every candidate selected
+    for (int j = tid; j < li.n; j += FIN_NT) out[j] = j;
+    return;
+  }
+  __shared__ uint32_t sh[3 * (FIN_NT / 64) + 3];
+  __shared__ uint32_t hist2[2048];
+  __shared__ uint32_t bits[CAND_MAX_WORDS];
+  __shared__ uint32_t s_cut;
+  const uint32_t* w = ws_list(a, list);
+  const uint32_t nc = w[W_CCOUNT];
+  const uint2* cand = (const uint2*)(w + a.cand_off);
+  constexpr int CPT = 4;                                          // candidates per thread per batch
+  uint2 cr[CPT];
+  auto cload = [&](uint32_t i0) {                                 // clamped: in bounds, no branch
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) cr[u] = cand[min(i0 + u * FIN_NT + tid, max(nc, 1u) - 1u)];
+  };
+  auto for_cand = [&](auto&& f) {                                 // f(key, index) over all candidates
+    for (uint32_t i0 = 0; i0 < nc; i0 += CPT * FIN_NT) {
+      if (i0 || nc > CPT * FIN_NT) cload(i0);                     // else the registers hold them all
+#pragma unroll
+      for (int u = 0; u < CPT; ++u)
+        if (i0 + u * FIN_NT + tid < nc) f(cr[u].x, cr[u].y);
+    }
+  };
+  cload(0);                                                       // in flight during the first digit
+  for (int i = tid; i < 2048; i += FIN_NT) hist2[i] = 0u;
+  uint32_t b1, rem1, b2, rem2, b3, rem3;
+  find_digit<FIN_NT, 2048>(w + W_HIST1, (uint32_t)li.kk, sh, b1, rem1);   // (its barriers order hist2's clear)
+  for_cand([&](uint32_t key, uint32_t) {
+    if (((key >> 20) & 0x7FFu) == b1) atomicAdd(&hist2[(key >> 9) & 0x7FFu], 1u);
+  });
+  __syncthreads();
+  find_digit<FIN_NT, 2048>(hist2, rem1, sh, b2, rem2);
+  for (int i = tid; i < 512; i += FIN_NT) hist2[i] = 0u;          // third digit: 9 bits
+  __syncthreads();
+  const uint32_t hi = 0x400000u | (b1 << 11) | b2;                // key bits 31..9
+  for_cand([&](uint32_t key, uint32_t) {
+    if ((key >> 9) == hi) atomicAdd(&hist2[key & 0x1FFu], 1u);
+  });
+  __syncthreads();
+  find_digit<FIN_NT, 512>(hist2, rem2, sh, b3, rem3);
+  const uint32_t T = (hi << 9) | b3;
+  const uint32_t need = rem3;                                     // keys == T taken, lowest index first
+  const uint32_t ties = hist2[b3];
+  const int nw = (li.n + 31) / 32;
+  const int wpt = (nw + FIN_NT - 1) / FIN_NT;                     // bitmap words per thread (contiguous)
+  uint32_t cut = 0xFFFFFFFFu;                                     // ties with index <= cut are taken
+  if (need < ties) {
+    for (int i = tid; i < nw; i += FIN_NT) bits[i] = 0u;
+    __syncthreads();
+    for_cand([&](uint32_t key, uint32_t j) {
+      if (key == T) atomicOr(&bits[j >> 5], 1u << (j & 31));
+    });
+    __syncthreads();
+    uint32_t cnt = 0;
+    for (int i = 0; i < wpt; ++i) {
+      const int wi = tid * wpt + i;
+      if (wi < nw) cnt += __builtin_popcount(bits[wi]);
+    }
+    uint32_t tot;
+    uint32_t before = block_scan_excl<FIN_NT>(cnt, sh, tot, false);
+    if (before < need && need <= before + cnt) {                  // this thread holds the need-th tie
+      for (int i = 0; i < wpt; ++i) {
+        const int wi = tid * wpt + i;
+        uint32_t x = wi < nw ? bits[wi] : 0u;
+        const uint32_t c = __builtin_popcount(x);
+        if (before + c >= need) {
+          for (uint32_t r = need - before; r > 1; --r) x &= x - 1u;   // drop the lower set bits
+          s_cut = (uint32_t)wi * 32u + (uint32_t)__builtin_ctz(x);
+          break;
+        }
+        before += c;
+      }
+    }
+    __syncthreads();
+    cut = s_cut;
+  }
+  for (int i = tid; i < nw; i += FIN_NT) bits[i] = 0u;
+  __syncthreads();
+  for_cand([&](uint32_t key, uint32_t j) {
+    if (key > T || (key == T && j <= cut)) atomicOr(&bits[j >> 5], 1u << (j & 31));
+  });
+  __syncthreads();
+  uint32_t cnt = 0;
+  for (int i = 0; i < wpt; ++i) {
+    const int wi = tid * wpt + i;
+    if (wi < nw) cnt += __builtin_popcount(bits[wi]);
+  }
+  uint32_t tot;
+  uint32_t pos = block_scan_excl<FIN_NT>(cnt, sh, tot, false);
+  for (int i = 0; i < wpt; ++i) {
+    const int wi = tid * wpt + i;
+    uint32_t x = wi < nw ? bits[wi] : 0u;
+    while (x) {
+      const int bit = __builtin_ctz(x);
+      if (pos < (uint32_t)li.kk) out[pos] = wi * 32 + bit;
+      ++pos;
+      x &= x - 1u;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- block-level variant (HySparse v1)
 //
 // dpshk page, section 03: the previous generation chose history in 64-token blocks.  Block b
@@ -442,7 +568,13 @@ hipError_t launch_select_blocks(const SelectArgs& a, int n_lists, int64_t max_ca
 
 int64_t select_blocks_max_candidates() { return (int64_t)MAX_BLOCKS * BLK; }
 
+hipError_t launch_select_cand(const SelectArgs& a, int n_lists, hipStream_t st) {
+  hipLaunchKernelGGL(sel_cand_select_kernel, dim3(n_lists), dim3(FIN_NT), 0, st, a);
+  return hipGetLastError();
+}
+
 static_assert(W_ZERO == SELECT_ZERO_WORDS, "cleared words of the selection workspace");
+static_assert(W_CCOUNT == SELECT_CCOUNT_WORD, "candidate count word of the selection workspace");
 
 hipError_t launch_select(const SelectArgs& a, int n_lists, bool fused_prefix, hipStream_t st) {
   const dim3 g(a.max_chunks, n_lists);

@@ -30,6 +30,44 @@ __device__ __forceinline__ void zero_hook(const AttnArgs& a) {
   zero_words_grid(a.zero_ptr, a.zero_stride, a.zero_words, a.zero_lists);
 }
 
+// First digit of a score's key in candidate mode: key bits 30..20 (8 exponent and 3 fraction bits,
+// eighth-octave bins).  The score pass only produces scores >= +0, whose keys all have bit 31 set,
+// so these bits order them.
+__device__ __forceinline__ int cand_digit(uint32_t key) { return (int)((key >> 20) & 0x7FFu); }
+
+// Lowest candidate-mode first digit that the kk-th largest key of a list can still have, from the
+// list's histogram as it stands: the highest digit d whose bins >= d already hold kk keys (counts
+// only grow while the pass runs, so the final kk-th key's digit is >= d); 0 while fewer than kk
+// keys have been counted.  Scores are sums of at most 32 probabilities; the bins of values in
+// [2^-55, 2^17), digits 576 .. 1151, are read, 9 per lane, with device-coherent loads (keys outside
+// them could only make d lower, never wrong).  Whole wave.
+__device__ int lower_digit(const uint32_t* hist, uint32_t kk, int lane) {
+  constexpr int PL = 9;
+  uint32_t h[PL], tot = 0;
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    h[i] = __hip_atomic_load(hist + 576 + PL * lane + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    tot += h[i];
+  }
+  uint32_t suf = tot;                                             // keys in this lane's bins and above
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_down(suf, o);
+    if (lane + o < 64) suf += y;
+  }
+  const unsigned long long reach = __ballot(suf >= kk);           // lanes 0 .. top reach kk
+  if (!reach) return 0;
+  const int top = 63 - __clzll((long long)reach);                 // highest such lane
+  uint32_t above = __shfl(suf - tot, top);
+  int found = 0;                                                  // bins of lane `top` from its top one
+#pragma unroll
+  for (int i = PL - 1; i >= 0; --i) {
+    above += h[i];
+    found += above < kk ? 1 : 0;
+  }
+  return 576 + PL * top + (PL - 1) - __shfl(found, top);
+}
+
 }  // namespace
 
 template <int KVT, int NW>
@@ -255,7 +293,14 @@ __global__ __launch_bounds__(64 * NW) void attn_wave_kernel(AttnArgs a) {
 // two tiles in flight in registers while the current one, staged in the
 // wave's own LDS slice, feeds the MFMA B operand (S = Q K^T: lane = token, 16
 // rows per lane), so the sum over a query token's heads is mostly in-lane.
-template <int KVT, int NW, int NQ>
+//
+// CAND (candidate mode, one query token): the grid holds about one workgroup per CU and each
+// keeps one list, walking its items of a.chunk = 2 NW TT tokens chunk-major (item j is the list's
+// chunk slot + j * nper), so every list's histogram fills early in the pass.  After each item a
+// wave moves its share of the LDS histogram to the list's global one and, on its turn, derives
+// from it the lowest first digit the k'-th key can still have; the scores at or above it are
+// appended as (key, index) pairs for the selection, and dense scores are written only on request.
+template <int KVT, int NW, int NQ, bool CAND>
 __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
   constexpr bool FP8 = KVT == KV_FP8;
   constexpr int NT = 64 * NW;
@@ -270,11 +315,20 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
   __shared__ float ksc[FP8 ? NW : 1][TT];
 
   __shared__ float s_lse2[32];
+  __shared__ int s_kd;                                           // CAND: lowest first digit appended
+  static_assert(!CAND || NQ == 1, "candidate mode: one query token");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int list, cidx;                                                // lists own max(fold, ceil(ncand / chunk)) items
-  grid_item(a.seq_len, a.n_kv, a.n_lists, a.chunk, a.window, a.part_ml ? 1 : 0, a.uniform_items, blockIdx.x, list,
-            cidx);
-  if (list < 0) return;
+  int list, cidx, slot = 0, nper = 1;                            // lists own max(fold, ceil(ncand / chunk)) items
+  if constexpr (CAND) {
+    list = (int)blockIdx.x % a.n_lists;
+    slot = (int)blockIdx.x / a.n_lists;
+    nper = (int)gridDim.x / a.n_lists;                           // workgroups per list
+    cidx = slot;
+  } else {
+    grid_item(a.seq_len, a.n_kv, a.n_lists, a.chunk, a.window, a.part_ml ? 1 : 0, a.uniform_items, blockIdx.x, list,
+              cidx);
+    if (list < 0) return;
+  }
   const int g = list % a.n_kv, b = list / a.n_kv;
   const int Lb = a.seq_len[b];
   const int w = min(a.window, Lb);
@@ -285,31 +339,40 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
   const char* kbase = (const char*)a.k + ((size_t)rs * a.n_kv + g) * SB;
   const size_t rstride = (size_t)a.n_kv * SB;
   const int ntiles = c1 > c0 ? (c1 - c0 + TT - 1) / TT : 0;
+  // This wave's tiles q = 0 .. nq - 1 by first token; positions from cend on are masked (a CAND tile
+  // never crosses its item, whose tiles wave and wave + NW are this wave's q = 2j and 2j + 1).
+  const int nitem_all = CAND ? (ncand + a.chunk - 1) / a.chunk : 0;
+  const int nq = CAND ? (slot < nitem_all ? 2 * ((nitem_all - 1 - slot) / nper + 1) : 0)
+                      : (wave < ntiles ? (ntiles - 1 - wave) / NW + 1 : 0);
+  const int cend = CAND ? ncand : c1;
+  auto tstart = [&](int q) -> int {
+    if constexpr (CAND) return (slot + (q >> 1) * nper) * a.chunk + (wave + NW * (q & 1)) * TT;
+    else return c0 + (wave + NW * q) * TT;
+  };
   char* const kt = ktile[wave];
   // Two tiles in flight per wave: buffers A and B alternate (named, so every wait is a static count).
   // Loads are clamped to the wave's last tile instead of skipped, so no branch surrounds a load; the
   // repeated tile at the end hits in cache.
   u32x4 kA[PPL], kB[PPL];
   float sA = 0.f, sB = 0.f;
-  auto load = [&](u32x4 (&kr)[PPL], float& ks, int tile) {      // clamped rows: no branch, in bounds
+  auto load = [&](u32x4 (&kr)[PPL], float& ks, int ts) {        // clamped rows: no branch, in bounds
 #pragma unroll
     for (int i = 0; i < PPL; ++i) {
       const int p = lane + 64 * i;
-      const int pos = min(c0 + tile * TT + p / PPR, c1 - 1);
+      const int pos = min(ts + p / PPR, cend - 1);
       kr[i] = *(const u32x4*)(kbase + (size_t)pos * rstride + (p % PPR) * 16);
     }
-    if (FP8) ks = a.k_scale[((size_t)rs + min(c0 + tile * TT + lane, c1 - 1)) * a.n_kv + g];
+    if (FP8) ks = a.k_scale[((size_t)rs + min(ts + lane, cend - 1)) * a.n_kv + g];
   };
-  const int last = wave + NW * (max(ntiles - 1 - wave, 0) / NW);  // this wave's last tile
-  if (wave < ntiles) {                                           // in flight during the prologue below
-    load(kA, sA, wave);
-    load(kB, sB, min(wave + NW, last));
+  if (nq > 0) {                                                  // in flight during the prologue below
+    load(kA, sA, tstart(0));
+    load(kB, sB, tstart(min(1, nq - 1)));
   }
   if (a.part_ml) {
     // The full layer's merge, folded in (at most 64 chunks): every workgroup derives the LSE of all rows
     // from the chunk partials; row r's output is merged by workgroup r % nwg of the list's nwg >= 1.
     const int nchd = (Lb + a.dchunk - 1) / a.dchunk;
-    const int nwg = max(1, (ncand + a.chunk - 1) / a.chunk);
+    const int nwg = CAND ? nper : max(1, (ncand + a.chunk - 1) / a.chunk);
     if (cidx >= nwg) return;
     const size_t first = (size_t)list * a.dmax_chunks * a.R;
     for (int r = wave; r < a.R; r += NW) {
@@ -325,10 +388,17 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
       if (lane == 0 && a.lse) a.lse[orow] = l2 * LN2;
     }
   }
-  if (c0 >= ncand) return;
+  if (!CAND && c0 >= ncand) return;
   const bool do_hist = a.hist != nullptr;
   if (do_hist)
     for (int i = tid; i < NQ * 2048; i += NT) hist[i >> 11][i & 2047] = 0u;
+  const int kk = max(0, min(a.top_k, Lb - a.window));
+  const bool need_cand = CAND && kk > 0 && kk < ncand;           // else the selection needs no candidates
+  uint32_t* ghist = a.hist + ((size_t)b * a.n_kv + g) * a.hist_stride;   // CAND: the list's (one query token)
+  if (CAND && wave == 0) {
+    const int d = need_cand ? lower_digit(ghist, (uint32_t)kk, lane) : 2048;
+    if (lane == 0) s_kd = d;
+  }
   for (int p = tid; p < 32 * 16; p += NT) {
     const int r = p >> 4, c = p & 15;
     u32x4 x = {0u, 0u, 0u, 0u};
@@ -355,8 +425,8 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
     lse2[r] = rw < a.R ? v : INFINITY;
   }
   const int tpw = a.G >= 32 ? 1 : 32 / a.G;                      // query tokens in the 32 rows
-  float* sout = a.scores + (size_t)b * a.n_q * a.n_kv * a.s_stride;
-  auto process = [&](const u32x4 (&kr)[PPL], float ks, int tile) {
+  float* sout = a.scores ? a.scores + (size_t)b * a.n_q * a.n_kv * a.s_stride : nullptr;
+  auto process = [&](const u32x4 (&kr)[PPL], float ks, int ts) {
     wave_sync();
 #pragma unroll
     for (int i = 0; i < PPL; ++i) {                              // registers -> LDS (FP8 -> bf16)
@@ -394,7 +464,7 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
       float p[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) p[r] = exp2_fast(s[r] * f - lse2[r]);
-      const int pos = c0 + tile * TT + 32 * half + (lane & 31);
+      const int pos = ts + 32 * half + (lane & 31);
       float tv[NQ];
       if (tpw == 1) {
         float v = 0.f;
@@ -411,23 +481,50 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
 #pragma unroll
         for (int t = 0; t < NQ; ++t) tv[t] = tpw == 4 ? blk[t] : blk[2 * t] + blk[2 * t + 1];
       }
-      if (lane < 32 && pos < c1) {
+      if (lane < 32 && pos < cend) {
 #pragma unroll
         for (int t = 0; t < NQ; ++t) {
           if (t >= a.n_q) break;
-          sout[((size_t)t * a.n_kv + g) * a.s_stride + pos] = tv[t];
-          if (do_hist) atomicAdd(&hist[t][f32_key(tv[t]) >> 21], 1u);
+          if (sout) sout[((size_t)t * a.n_kv + g) * a.s_stride + pos] = tv[t];
+          if (do_hist) atomicAdd(&hist[t][CAND ? cand_digit(f32_key(tv[t])) : (int)(f32_key(tv[t]) >> 21)], 1u);
+        }
+      }
+      if (need_cand) {                                           // append (key, index): one reservation per wave
+        const uint32_t key = f32_key(tv[0]);
+        const bool keep = lane < 32 && pos < cend && cand_digit(key) >= *(volatile int*)&s_kd;
+        const unsigned long long mk = __ballot(keep);
+        if (mk) {
+          uint32_t base = 0u;
+          if (lane == 0) base = atomicAdd(ghist + SELECT_CCOUNT_WORD, (uint32_t)__popcll(mk));
+          base = __shfl(base, 0);
+          if (keep)
+            ((uint2*)(ghist + a.cand_off))[base + __popcll(mk & ((1ull << lane) - 1ull))] = make_uint2(key, (uint32_t)pos);
         }
       }
     }
   };
-  if (wave < ntiles) {
-    for (int tile = wave; tile < ntiles; tile += 2 * NW) {
-      process(kA, sA, tile);
-      load(kA, sA, min(tile + 2 * NW, last));
-      if (tile + NW >= ntiles) break;
-      process(kB, sB, tile + NW);
-      load(kB, sB, min(tile + 3 * NW, last));
+  for (int q = 0; q < nq; q += 2) {
+    process(kA, sA, tstart(q));
+    load(kA, sA, tstart(min(q + 2, nq - 1)));                    // past the end: the last tile again (cache hit)
+    if (q + 1 >= nq) break;
+    process(kB, sB, tstart(q + 1));
+    // on this wave's turn, a fresh bound from the list's histogram (here, while kB's registers are
+    // free; the next load of kB waits for it)
+    if (need_cand && (q >> 1) % NW == wave) {
+      const int d = lower_digit(ghist, (uint32_t)kk, lane);
+      if (lane == 0) atomicMax(&s_kd, d);
+    }
+    load(kB, sB, tstart(min(q + 3, nq - 1)));
+    if (need_cand) {
+      // this wave's share of the histogram to the list's global one (read and clear: adds that other
+      // waves make meanwhile stay for a later move), only its bins at or above the current bound: the
+      // bound never falls, so lower bins cannot move it (they reach the global histogram at the end)
+      constexpr int SHARE = 2048 / NW;
+      const int lo = max(wave * SHARE, *(volatile int*)&s_kd);
+      for (int i = lo + lane; i < (wave + 1) * SHARE; i += 64) {
+        const uint32_t v = atomicExch(&hist[0][i], 0u);
+        if (v) atomicAdd(ghist + i, v);
+      }
     }
   }
   if (!do_hist) return;
@@ -455,12 +552,21 @@ hipError_t launch_attn_wave(const AttnArgs& a, int kvt, hipStream_t st) {
 template <int KVT, int NQ>
 static void launch_scores_wave_t(const ScoreArgs& a, hipStream_t st) {
   constexpr int NW = NQ == 1 ? 8 : 6;                            // LDS: NW x 17 KB tiles + NQ x 8 KB histograms
-  dim3 grid(a.n_items, 1, 1);
-  hipLaunchKernelGGL((scores_wave_kernel<KVT, NW, NQ>), grid, dim3(64 * NW), 0, st, a);
+  if constexpr (NQ == 1) {
+    if (a.cand_off > 0) {
+      hipLaunchKernelGGL((scores_wave_kernel<KVT, NW, NQ, true>), dim3(a.n_items), dim3(64 * NW), 0, st, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((scores_wave_kernel<KVT, NW, NQ, false>), dim3(a.n_items), dim3(64 * NW), 0, st, a);
 }
+
+int scores_cand_chunk() { return 2 * 8 * 64; }
 
 hipError_t launch_scores_wave(const ScoreArgs& a, int kvt, hipStream_t st) {
   if (a.R > 32 || a.n_q > 4 || (kvt != KV_BF16 && kvt != KV_FP8)) return hipErrorInvalidValue;
+  if (a.cand_off > 0 && (a.n_q != 1 || !a.hist || a.chunk != scores_cand_chunk() || a.n_items % a.n_lists))
+    return hipErrorInvalidValue;
   const int nq = a.n_q == 1 ? 1 : a.n_q == 2 ? 2 : 4;
   if (kvt == KV_BF16) {
     if (nq == 1) launch_scores_wave_t<KV_BF16, 1>(a, st);

@@ -140,3 +140,44 @@ def test_select_blocks_budgets_and_long_list():
     x = (rng.random(L - 128) * 1e-4).astype(np.float32)
     x[rng.choice(L - 128, 300, replace=False)] = np.float32(5e-3)
     _check_blocks(x.reshape(1, 1, 1, -1), [L], 1, 1, 1024, 128)
+
+
+@pytest.mark.parametrize("n_q,H,L", [(1, 32, 40000), (1, 32, 1153), (1, 32, 300), (2, 16, 40000)])
+def test_candidate_selection_paths_agree(n_q, H, L, monkeypatch):
+    """The full layer's selection three ways: from the candidates the score pass appends (the
+    default for one query token and equal lengths; no dense scores stored), the same with the
+    dense scores requested, and the dense three-kernel radix select.  All give identical lists,
+    and the one with scores equals the oracle's selection on those scores.  L = 1153 leaves most
+    score workgroups without an item, L = 300 selects every candidate; the last sequence has
+    identical K rows, so every score ties and the lowest indices must win."""
+    import synth
+    from long_context_split_amd import hysparse as hs
+    banner(f"candidate vs dense selection n_q={n_q} H={H} L={L}")
+    rng = np.random.default_rng(21 + n_q + L)
+    B = 5
+    lens = [L] * B
+    k = rng.standard_normal((B * L, 1, 128)).astype(np.float32)
+    k[(B - 1) * L:] = k[(B - 1) * L]                              # identical rows: all scores tied
+    v = rng.standard_normal((B * L, 1, 128)).astype(np.float32)
+    q = rng.standard_normal((B, n_q, H, 128)).astype(np.float32)
+    dev = lambda x: torch.from_numpy(synth.bf16_bits(x).view(np.int16)).cuda().view(torch.bfloat16)
+    kv = hs.KVCache(dev(k), dev(v), lens)
+    qd = dev(q)
+    _, _, idx_a, cnt_a = hs.full_attn_select(kv, qd)
+    S = hs.scores_stride(kv, 128)
+    sc = torch.empty((B, n_q, 1, S), dtype=torch.float32, device="cuda")
+    _, _, idx_b, cnt_b = hs.full_attn_select(kv, qd, scores_out=sc)
+    monkeypatch.setenv("HS_DENSE_SELECT", "1")
+    _, _, idx_c, cnt_c = hs.full_attn_select(kv, qd)
+    torch.cuda.synchronize()
+    ia, ib, ic = idx_a.cpu().numpy(), idx_b.cpu().numpy(), idx_c.cpu().numpy()
+    assert np.array_equal(ia, ib) and np.array_equal(ia, ic)
+    assert np.array_equal(cnt_a.cpu().numpy(), cnt_c.cpu().numpy())
+    scores = sc.cpu().numpy()
+    w, kk = selection.budget(L, 1024, 128)
+    for i in range(B):
+        for t in range(n_q):
+            gi, gc = selection.select(np.ascontiguousarray(scores[i, t, 0, :L - w]), L, 1024, 128, f32_keys=True)
+            assert np.array_equal(ia[i, t, 0], gi), f"seq {i} t {t}"
+    last = ia[-1, :, 0, :kk]
+    assert np.array_equal(last, np.broadcast_to(np.arange(kk), last.shape))
