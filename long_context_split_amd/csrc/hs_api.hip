@@ -161,6 +161,10 @@ struct FullPlan {
   int ct, nwr, G, R, n_lists, chunk, max_chunks;
   int nwr_s, chunk_s, max_chunks_s;
   int64_t s_stride;
+  // candidate mode (one query token, equal lengths, wave path): score workgroups (about one per
+  // CU, a multiple of the lists), each filling its own region of cand_region pairs
+  int cand, cand_wgs;
+  int64_t cand_region;
   size_t off_acc, off_ml, off_lse2, off_scores, off_sel, total;
   hs::SelectPlan sel;
 };
@@ -240,7 +244,21 @@ hs_status plan_full(const hs_kv_cache* kv, const hs_attn_params* p, hs_dtype q_d
   off += align_up((size_t)ci.B * p->q_tokens * H * 4, 256);
   pl.off_scores = off;
   off += align_up((size_t)ci.B * p->q_tokens * ci.n_kv * pl.s_stride * 4, 256);
-  hs::select_plan(pl.s_stride, pl.sel);
+  bool equal_len = true;
+  for (int b = 1; b < ci.B; ++b) equal_len = equal_len && kv->h_seq_len[b] == kv->h_seq_len[0];
+  pl.cand = pl.wave && p->q_tokens == 1 && equal_len && p->select_block == 0 &&
+            pl.s_stride <= hs::SELECT_CAND_MAX_N && !env_int("HS_DENSE_SELECT", 0);
+  pl.cand_wgs = 0;
+  pl.cand_region = 0;
+  int64_t cand_pairs = 0;
+  if (pl.cand) {
+    const int nper = std::max(1, 256 / pl.n_lists);               // score workgroups per list
+    const int64_t items = (pl.s_stride + hs::scores_cand_chunk() - 1) / hs::scores_cand_chunk();
+    pl.cand_wgs = pl.n_lists * nper;
+    pl.cand_region = (items + nper - 1) / nper * hs::scores_cand_chunk();
+    cand_pairs = pl.cand_region * nper;
+  }
+  hs::select_plan(pl.s_stride, pl.sel, cand_pairs);
   pl.off_sel = off;
   off += align_up((size_t)ci.B * p->q_tokens * ci.n_kv * pl.sel.ws_stride * 4, 256);
   pl.total = off;
@@ -467,13 +485,9 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
   m.gather = 0; m.n_kv = ci.n_kv; m.H = a.H; m.G = pl.G; m.n_q = a.n_q; m.R = pl.R; m.n_lists = pl.n_lists;
   m.chunk = pl.chunk; m.max_chunks = pl.max_chunks; m.out = out; m.lse = lse; m.lse2 = lse2;
   const bool fold_merge = pl.wave && !a.direct && pl.max_chunks <= 64;   // scores_wave merges O, writes LSE
-  // candidate mode (scores_wave, one query token, equal lengths): the score pass appends the pairs
-  // that can still reach the k'-th key and the selection runs on them in one workgroup per list;
-  // dense scores only on request
-  bool equal_len = true;
-  for (int b = 1; b < ci.B; ++b) equal_len = equal_len && kv->h_seq_len[b] == kv->h_seq_len[0];
-  const bool cand_mode = pl.wave && p->q_tokens == 1 && equal_len && p->select_block == 0 &&
-                         pl.s_stride <= hs::SELECT_CAND_MAX_N && !env_int("HS_DENSE_SELECT", 0);
+  // candidate mode: the score pass appends the pairs that can still reach the k'-th key and the
+  // selection runs on them in one workgroup per list; dense scores only on request
+  const bool cand_mode = pl.cand;
   if (!a.direct && !fold_merge)                                   // several chunks: merge them
     if ((e = timed("attn_merge_dense", s, [&] { return hs::launch_attn_merge(m, s); })) != hipSuccess)
       return hip_fail(e, "full attention merge");
@@ -503,9 +517,10 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
       if (cand_mode) {                                            // about one workgroup per CU, each on one list
         sa.scores = scores_out;                                   // nullable: the test hook only
         sa.cand_off = pl.sel.cand_off;
+        sa.cand_region = pl.cand_region;
         sa.top_k = p->top_k;
         sa.chunk = hs::scores_cand_chunk();
-        sa.n_items = pl.n_lists * std::max(1, 256 / pl.n_lists);
+        sa.n_items = pl.cand_wgs;
       }
       if (sa.n_items > 0 &&
           (e = timed("scores_wave", s, [&] { return hs::launch_scores_wave(sa, kvt, s); })) != hipSuccess)
@@ -522,6 +537,7 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
   se.sel_idx = sel_idx; se.sel_count = sel_count;
   se.ws = (uint32_t*)(ws + pl.off_sel); se.ws_stride = pl.sel.ws_stride; se.cand_off = pl.sel.cand_off;
   se.chunk = pl.sel.chunk; se.max_chunks = pl.sel.max_chunks;
+  se.cand_regions = pl.cand ? pl.cand_wgs / pl.n_lists : 0; se.cand_region = pl.cand_region;
   if (p->select_block == 64)
     e = timed("select_blocks", s, [&] { return hs::launch_select_blocks(se, n_sel_lists, pl.s_stride, s); });
   else if (cand_mode)

@@ -81,9 +81,11 @@ struct ScoreArgs {
   // scores_cand_chunk(), n_items = workgroups, a multiple of n_lists): workgroup w keeps list
   // w % n_lists and appends the (key, index) pairs of every score whose first digit is at or
   // above the lowest digit the k'-th key can still have (from the list's histogram as it fills)
-  // to the list's candidate buffer (hist + cand_off words, count at SELECT_CCOUNT_WORD);
-  // `scores` may then be null (no dense scores written)
+  // to its own region of the list's candidate buffer (hist + cand_off words; region w / n_lists of
+  // cand_region pairs, its pair count written at SELECT_RCOUNT_WORD + w / n_lists); `scores` may
+  // then be null (no dense scores written)
   int64_t cand_off;
+  int64_t cand_region;
   int top_k;
 };
 
@@ -97,13 +99,16 @@ struct SelectArgs {
   uint32_t* ws;          // [lists][ws_stride] words (layout in hs_select.hip)
   int64_t ws_stride, cand_off;
   int chunk, max_chunks; // candidates per chunk workgroup, chunks per list
+  int cand_regions;      // candidate mode: regions of cand_region pairs per list (one per score workgroup),
+  int64_t cand_region;   //   their pair counts at SELECT_RCOUNT_WORD
 };
 
 struct SelectPlan {
   int chunk, max_chunks;
   int64_t ws_stride, cand_off;   // words
 };
-void select_plan(int64_t s_stride, SelectPlan& p);
+// cand_pairs: candidate-mode capacity (pairs per list) when it exceeds s_stride
+void select_plan(int64_t s_stride, SelectPlan& p, int64_t cand_pairs = 0);
 
 struct BridgeArgs {
   const uint16_t* x;     // [T, D] bf16
@@ -167,6 +172,7 @@ hipError_t launch_scores_wave(const ScoreArgs& a, int kvt, hipStream_t st);
 int scores_cand_chunk();
 constexpr int SELECT_ZERO_WORDS = 4100;   // per-list words the selection needs cleared
 constexpr int SELECT_CCOUNT_WORD = 4096;  // per-list word: candidate pairs appended so far
+constexpr int SELECT_RCOUNT_WORD = 2048;  // candidate mode: per-list pair counts of the regions (<= 256)
 // candidate mode: the score pass appended the candidate pairs (ScoreArgs::cand_off); one workgroup
 // per list, lists of at most SELECT_CAND_MAX_N candidates (an LDS bitmap over them)
 constexpr int SELECT_CAND_MAX_N = 1 << 20;

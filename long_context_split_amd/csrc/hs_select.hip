@@ -340,8 +340,9 @@ __global__ __launch_bounds__(CH_NT) void sel_write_kernel(SelectArgs a) {
 // ---------------------------------------------------------------- candidate mode
 //
 // The score pass appended, per list, the (key, index) pairs of every score whose first digit could
-// still reach the k'-th key (all pairs of the boundary digit and above, in no particular order) and
-// built the full first-digit histogram.  Its scores are >= +0, so every key has bit 31 set and the
+// still reach the k'-th key (all pairs of the boundary digit and above, in no particular order; each
+// score workgroup fills its own region of the list's buffer and records its count) and built the
+// full first-digit histogram.  Its scores are >= +0, so every key has bit 31 set and the
 // digits are bits 30..20, 19..9 and 8..0.  One workgroup per list:
 //   * first digit from the histogram; the second and third digits from the candidates in the
 //     boundary bin -> the exact k'-th key T and the number `need` of keys equal to T taken;
@@ -368,27 +369,70 @@ __global__ __launch_bounds__(FIN_NT) void sel_cand_select_kernel(SelectArgs a) {
   __shared__ uint32_t hist2[2048];
   __shared__ uint32_t bits[CAND_MAX_WORDS];
   __shared__ uint32_t s_cut;
+  __shared__ uint32_t rcnt[256];                                  // pairs in each region
+  __shared__ uint32_t s_maxc;
   const uint32_t* w = ws_list(a, list);
-  const uint32_t nc = w[W_CCOUNT];
   const uint2* cand = (const uint2*)(w + a.cand_off);
-  constexpr int CPT = 4;                                          // candidates per thread per batch
-  uint2 cr[CPT];
-  auto cload = [&](uint32_t i0) {                                 // clamped: in bounds, no branch
+  const int nreg = a.cand_regions;                                // <= 256
+  if (tid == 0) s_maxc = 1u;
+  __syncthreads();
+  if (tid < nreg) {
+    const uint32_t c = w[SELECT_RCOUNT_WORD + tid];
+    rcnt[tid] = c;
+    atomicMax(&s_maxc, c);
+  }
+  __syncthreads();
+  // positions p in [0, nreg * maxc): region p / maxc, slot p % maxc, a pair when the slot is below
+  // the region's count; addresses need no search, so the loads of a batch go out together
+  const uint32_t maxc = s_maxc, npos = (uint32_t)nreg * maxc;
+  const float rmaxc = 1.0f / (float)maxc;
+  // Positions in batches of CPT per thread.  Batches 0 and 1 are loaded once and stay in registers
+  // for every pass (lists of up to 2 * BATCH positions never reload); longer lists reload their
+  // later batches in every pass, issuing them before the pass works through batch 0.
+  constexpr int CPT = 16;                                         // positions per thread per batch
+  constexpr uint32_t BATCH = CPT * FIN_NT;
+  auto cload = [&](uint2 (&cr)[CPT], uint32_t& cv, uint32_t i0) {  // clamped: in bounds, no branch
+    cv = 0u;
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) cr[u] = cand[min(i0 + u * FIN_NT + tid, max(nc, 1u) - 1u)];
-  };
-  auto for_cand = [&](auto&& f) {                                 // f(key, index) over all candidates
-    for (uint32_t i0 = 0; i0 < nc; i0 += CPT * FIN_NT) {
-      if (i0 || nc > CPT * FIN_NT) cload(i0);                     // else the registers hold them all
-#pragma unroll
-      for (int u = 0; u < CPT; ++u)
-        if (i0 + u * FIN_NT + tid < nc) f(cr[u].x, cr[u].y);
+    for (int u = 0; u < CPT; ++u) {
+      const uint32_t p = i0 + u * FIN_NT + tid, pc = min(p, npos - 1u);
+      uint32_t r = (uint32_t)((float)pc * rmaxc);                // pc < 2^24: off by at most one
+      r -= r * maxc > pc ? 1u : 0u;
+      r += (r + 1u) * maxc <= pc ? 1u : 0u;
+      const uint32_t j = pc - r * maxc;
+      cr[u] = cand[(size_t)r * a.cand_region + j];
+      cv |= (p < npos && j < rcnt[r] ? 1u : 0u) << u;
     }
   };
-  cload(0);                                                       // in flight during the first digit
-  for (int i = tid; i < 2048; i += FIN_NT) hist2[i] = 0u;
+  uint2 c0[CPT], c1[CPT];
+  uint32_t v0 = 0u, v1 = 0u;
+  const bool resident = npos <= 2 * BATCH;
+  auto for_cand = [&](auto&& f) {                                 // f(key, index) over all candidates
+    if (!resident) cload(c1, v1, BATCH);
+#pragma unroll
+    for (int u = 0; u < CPT; ++u)
+      if ((v0 >> u) & 1u) f(c0[u].x, c0[u].y);
+    for (uint32_t i0 = BATCH; i0 < npos; i0 += BATCH) {
+      if (i0 > BATCH) cload(c1, v1, i0);
+#pragma unroll
+      for (int u = 0; u < CPT; ++u)
+        if ((v1 >> u) & 1u) f(c1[u].x, c1[u].y);
+    }
+  };
+  // the first-digit histogram is loaded ahead of the candidates and searched in LDS, so the search
+  // does not wait for them
+  uint32_t h1[2048 / FIN_NT];
+#pragma unroll
+  for (int i = 0; i < 2048 / FIN_NT; ++i) h1[i] = w[W_HIST1 + i * FIN_NT + tid];
+  cload(c0, v0, 0);                                               // in flight during the first digit
+  if (resident && npos > BATCH) cload(c1, v1, BATCH);
+#pragma unroll
+  for (int i = 0; i < 2048 / FIN_NT; ++i) hist2[i * FIN_NT + tid] = h1[i];
+  __syncthreads();
   uint32_t b1, rem1, b2, rem2, b3, rem3;
-  find_digit<FIN_NT, 2048>(w + W_HIST1, (uint32_t)li.kk, sh, b1, rem1);   // (its barriers order hist2's clear)
+  find_digit<FIN_NT, 2048>(hist2, (uint32_t)li.kk, sh, b1, rem1);   // (ends with a barrier)
+  for (int i = tid; i < 2048; i += FIN_NT) hist2[i] = 0u;
+  __syncthreads();
   for_cand([&](uint32_t key, uint32_t) {
     if (((key >> 20) & 0x7FFu) == b1) atomicAdd(&hist2[(key >> 9) & 0x7FFu], 1u);
   });
@@ -589,12 +633,12 @@ hipError_t launch_select(const SelectArgs& a, int n_lists, bool fused_prefix, hi
 }
 
 // Chunking and workspace layout of the selection, shared with the host planner.
-void select_plan(int64_t s_stride, SelectPlan& p) {
+void select_plan(int64_t s_stride, SelectPlan& p, int64_t cand_pairs) {
   p.chunk = 4096;
   while ((s_stride + p.chunk - 1) / p.chunk > 1024) p.chunk *= 2;  // finalize handles <= 1024 chunks
   p.max_chunks = (int)std::max<int64_t>(1, (s_stride + p.chunk - 1) / p.chunk);
   p.cand_off = (W_CHUNKS + 4 * (int64_t)p.max_chunks + 1) & ~(int64_t)1;   // 8-byte aligned pairs
-  p.ws_stride = p.cand_off + 2 * std::max<int64_t>(s_stride, 1);
+  p.ws_stride = p.cand_off + 2 * std::max<int64_t>(std::max<int64_t>(s_stride, cand_pairs), 1);
 }
 
 }  // namespace hs

@@ -316,6 +316,7 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
 
   __shared__ float s_lse2[32];
   __shared__ int s_kd;                                           // CAND: lowest first digit appended
+  __shared__ uint32_t s_cc;                                      // CAND: pairs in this workgroup's region
   static_assert(!CAND || NQ == 1, "candidate mode: one query token");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int list, cidx, slot = 0, nper = 1;                            // lists own max(fold, ceil(ncand / chunk)) items
@@ -397,8 +398,9 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
   uint32_t* ghist = a.hist + ((size_t)b * a.n_kv + g) * a.hist_stride;   // CAND: the list's (one query token)
   if (CAND && wave == 0) {
     const int d = need_cand ? lower_digit(ghist, (uint32_t)kk, lane) : 2048;
-    if (lane == 0) s_kd = d;
+    if (lane == 0) { s_kd = d; s_cc = 0u; }
   }
+  uint2* const region = CAND ? (uint2*)(ghist + a.cand_off) + (size_t)slot * a.cand_region : nullptr;
   for (int p = tid; p < 32 * 16; p += NT) {
     const int r = p >> 4, c = p & 15;
     u32x4 x = {0u, 0u, 0u, 0u};
@@ -489,16 +491,15 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
           if (do_hist) atomicAdd(&hist[t][CAND ? cand_digit(f32_key(tv[t])) : (int)(f32_key(tv[t]) >> 21)], 1u);
         }
       }
-      if (need_cand) {                                           // append (key, index): one reservation per wave
+      if (need_cand) {                                           // append (key, index) to the workgroup's region
         const uint32_t key = f32_key(tv[0]);
         const bool keep = lane < 32 && pos < cend && cand_digit(key) >= *(volatile int*)&s_kd;
         const unsigned long long mk = __ballot(keep);
         if (mk) {
           uint32_t base = 0u;
-          if (lane == 0) base = atomicAdd(ghist + SELECT_CCOUNT_WORD, (uint32_t)__popcll(mk));
+          if (lane == 0) base = atomicAdd(&s_cc, (uint32_t)__popcll(mk));
           base = __shfl(base, 0);
-          if (keep)
-            ((uint2*)(ghist + a.cand_off))[base + __popcll(mk & ((1ull << lane) - 1ull))] = make_uint2(key, (uint32_t)pos);
+          if (keep) region[base + __popcll(mk & ((1ull << lane) - 1ull))] = make_uint2(key, (uint32_t)pos);
         }
       }
     }
@@ -529,6 +530,7 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
   }
   if (!do_hist) return;
   __syncthreads();
+  if (CAND && tid == 0) ghist[SELECT_RCOUNT_WORD + slot] = s_cc;
   for (int i = tid; i < a.n_q * 2048; i += NT) {
     const uint32_t v = hist[i >> 11][i & 2047];
     if (v) atomicAdd(a.hist + (((size_t)b * a.n_q + (i >> 11)) * a.n_kv + g) * a.hist_stride + (i & 2047), v);
