@@ -67,6 +67,7 @@ __global__ __launch_bounds__(64 * NRG) void attn_rows_kernel(AttnArgs a) {
   __shared__ __align__(16) char kt[TT * KROW];
   __shared__ __align__(16) char vt[D * VROW];
   __shared__ float ksc[FP8 ? TT : 1], vsc[FP8 ? TT : 1];
+  __shared__ float fmm[FP8 ? TT / 64 : 1][2];                    // per wave of the store: max, min logit factor
 
   zero_words_grid(a.zero_ptr, a.zero_stride, a.zero_words, a.zero_lists);   // the selection's histograms
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -151,13 +152,28 @@ __global__ __launch_bounds__(64 * NRG) void attn_rows_kernel(AttnArgs a) {
         *(uint32_t*)(vt + d * VROW + vt_quad<TT / 8>(d, col >> 3) + (col & 7) * 2) = word;
       }
     }
-    if (FP8 && tid < TT) { ksc[tid] = sk * sl2; vsc[tid] = sv; }   // logit factor: K scale x softmax scale
+    if (FP8 && tid < TT) {                                        // logit factor: K scale x softmax scale
+      const float f = sk * sl2;
+      ksc[tid] = f;
+      vsc[tid] = sv;
+      const float fx = wave_max(f), fn = -wave_max(-f);           // the super-tile's extreme factors
+      if (lane == 0) { fmm[wave][0] = fx; fmm[wave][1] = fn; }
+    }
     __syncthreads();
     prefetch(min(base + TT, last));                               // past the end: the last tile again (cache hit)
+    float fmax_t = sl2, fmin_t = sl2;
+    if (FP8) {
+#pragma unroll
+      for (int w = 0; w < TT / 64; ++w) { fmax_t = w ? fmaxf(fmax_t, fmm[w][0]) : fmm[w][0]; fmin_t = w ? fminf(fmin_t, fmm[w][1]) : fmm[w][1]; }
+    }
 
     // ---- each wave: its 32 rows against the NSUB 32-token sub-tiles.  Lazy rescaling: a row's
     // running max m moves only when a tile's max exceeds it by more than TAU (log2 units), so most
-    // tiles skip rescaling acc; p = 2^(x - m) <= 2^TAU stays well inside fp32 and bf16 range.
+    // tiles skip rescaling acc; p = 2^(x - m) <= 2^TAU stays well inside fp32 and bf16 range.  The
+    // tile max is taken on the raw products s and scaled by the super-tile's largest (smallest, for
+    // a negative max) logit factor: an upper bound of the true max, which is all the rescaling needs
+    // (m only has to stay at or above the logits, minus TAU; LSE = m + log2(l) is exact for any m),
+    // and the logits themselves are formed inside exp2's argument as fma(s, f, -m).
     constexpr float TAU = 8.f;
     auto tile = [&](int st, auto masked) {
       constexpr bool MASK = decltype(masked)::value;
@@ -172,27 +188,16 @@ __global__ __launch_bounds__(64 * NRG) void attn_rows_kernel(AttnArgs a) {
         }
       }
       // this lane's tokens crow(lane, 4k4 + i) = 32 st + 8 k4 + 4 (lane >> 5) + i: four runs of 4
-      float x[16], vs[16];
+      if (MASK) {
 #pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        const int t0 = 32 * st + 8 * k4 + 4 * (lane >> 5);
-        f32x4 f = {sl2, sl2, sl2, sl2};
-        if (FP8) {
-          f = *(const f32x4*)(ksc + t0);
-          const f32x4 v4 = *(const f32x4*)(vsc + t0);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) vs[4 * k4 + i] = v4[i];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[4 * k4 + i] = s[4 * k4 + i] * f[i];
-          if (MASK && base + t0 + i >= c1) x[4 * k4 + i] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (base + 32 * st + crow(lane, r) >= c1) s[r] = -INFINITY;
       }
-      float mt = x[0];
+      float smax = s[0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, x[r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      for (int r = 1; r < 16; ++r) smax = fmaxf(smax, s[r]);
+      smax = fmaxf(smax, __shfl_xor(smax, 32));
+      const float mt = smax * (smax >= 0.f ? fmax_t : fmin_t);      // >= the tile's max logit (log2 units)
       const bool need = mt > m + TAU;                               // same for both lanes of a row
       if (__ballot(need)) {
         const float mn = need ? mt : m;
@@ -204,10 +209,20 @@ __global__ __launch_bounds__(64 * NRG) void attn_rows_kernel(AttnArgs a) {
       }
       float p[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = exp2_fast(x[r] - m);
-        lsum += p[r];
-        if (FP8) p[r] *= vs[r];                                     // V scale folded into P
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const int t0 = 32 * st + 8 * k4 + 4 * (lane >> 5);
+        f32x4 f = {sl2, sl2, sl2, sl2}, v4 = {1.f, 1.f, 1.f, 1.f};
+        if (FP8) {
+          f = *(const f32x4*)(ksc + t0);
+          v4 = *(const f32x4*)(vsc + t0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * k4 + i;
+          p[r] = exp2_fast(fmaf(s[r], f[i], -m));
+          lsum += p[r];
+          if (FP8) p[r] *= v4[i];                                   // V scale folded into P
+        }
       }
       // P operand: k-step u, element j <-> p[8u + j] (token crow(lane, 8u + j))
       u32x4 ph[2], pl[2];
