@@ -198,32 +198,39 @@ __global__ __launch_bounds__(64 * NW) void attn_wave_kernel(AttnArgs a) {
                                                     0, 0, 0);
       }
     }
-    float l2[16];
+    // Online softmax in log2 units with lazy rescaling: a row's reference m moves only when the
+    // tile's max exceeds it by more than TAU, so p = 2^(l - m) <= 2^TAU and most tiles skip the
+    // rescale of acc (LSE = m + log2(l) and every later combination hold for any reference).  bf16:
+    // the factor is the constant sl2, so the max is taken on S and the logits are formed in exp2's
+    // fma; E4M3: per-token factors, logits formed first.
+    constexpr float TAU = 8.f;
     float mt = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int tk = crow(lane, r);
       const bool ok = c0 + tile * 32 + tk < c1;
-      float x = s[r] * sl2;
-      if (FP8) x *= wks[tk];
-      l2[r] = ok ? x : -INFINITY;
-      mt = fmaxf(mt, l2[r]);
+      const float x = FP8 ? s[r] * sl2 * wks[tk] : s[r];
+      s[r] = ok ? x : -INFINITY;
+      mt = fmaxf(mt, s[r]);
     }
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mn = fmaxf(m, mt);
-    const float msub = mn == -INFINITY ? 0.f : mn;
-    const float alpha = exp2f(m - msub);
+    if (!FP8) mt *= sl2;
+    const bool need = mt > m + TAU;                               // same for both lanes of a row
+    if (__ballot(need)) {                                         // every wave's first tile: m = -inf
+      const float mn = need ? mt : m;
+      const float alpha = exp2f(m - mn);
+      lsum *= alpha;
+#pragma unroll
+      for (int mt4 = 0; mt4 < 4; ++mt4) acc[mt4] *= alpha;
+      m = mn;
+    }
     float p[16];
-    lsum *= alpha;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      p[r] = exp2_fast(l2[r] - msub);
+      p[r] = exp2_fast(FP8 ? s[r] - m : fmaf(s[r], sl2, -m));
       lsum += p[r];
       if (FP8) p[r] *= wvs[crow(lane, r)];
     }
-    m = mn;
-#pragma unroll
-    for (int mt4 = 0; mt4 < 4; ++mt4) acc[mt4] *= alpha;
     M::template pv<SPLIT>(acc, vt, p, lane);
   }
   lsum += __shfl_xor(lsum, 32);
