@@ -246,7 +246,9 @@ hs_status plan_full(const hs_kv_cache* kv, const hs_attn_params* p, hs_dtype q_d
   off += align_up((size_t)ci.B * p->q_tokens * ci.n_kv * pl.s_stride * 4, 256);
   bool equal_len = true;
   for (int b = 1; b < ci.B; ++b) equal_len = equal_len && kv->h_seq_len[b] == kv->h_seq_len[0];
-  pl.cand = pl.wave && p->q_tokens == 1 && equal_len && p->select_block == 0 &&
+  // At least 16 lists: a list's score workgroups (256 / lists) store their first items unfiltered,
+  // which with fewer lists outweighs what candidate mode saves.
+  pl.cand = pl.wave && p->q_tokens == 1 && equal_len && p->select_block == 0 && pl.n_lists >= 16 &&
             pl.s_stride <= hs::SELECT_CAND_MAX_N && !env_int("HS_DENSE_SELECT", 0);
   pl.cand_wgs = 0;
   pl.cand_region = 0;
