@@ -255,9 +255,8 @@ hs_status plan_full(const hs_kv_cache* kv, const hs_attn_params* p, hs_dtype q_d
   int64_t cand_pairs = 0;
   if (pl.cand) {
     const int nper = std::max(1, 256 / pl.n_lists);               // score workgroups per list
-    const int64_t items = (pl.s_stride + hs::scores_cand_chunk() - 1) / hs::scores_cand_chunk();
     pl.cand_wgs = pl.n_lists * nper;
-    pl.cand_region = (items + nper - 1) / nper * hs::scores_cand_chunk();
+    pl.cand_region = hs::scores_cand_region(pl.s_stride, nper);
     cand_pairs = pl.cand_region * nper;
   }
   hs::select_plan(pl.s_stride, pl.sel, cand_pairs);

@@ -81,6 +81,10 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 // Orders a wave's own LDS writes before its later reads (and reads before later writes) of the
 // same wave-private buffer.
+// Read of cache rows that a pass streams once: a non-temporal load, so the lines do not
+// displace reused data in the caches on their way (on a 2.1 GB pass: 370 -> 327 us).
+__device__ __forceinline__ u32x4 load_stream(const void* p) { return __builtin_nontemporal_load((const u32x4*)p); }
+
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();

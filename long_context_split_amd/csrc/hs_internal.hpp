@@ -78,12 +78,13 @@ struct ScoreArgs {
   float* out;
   float* lse;            // nullable, natural log
   // scores_wave, candidate mode (cand_off > 0; one query token, hist set, chunk =
-  // scores_cand_chunk(), n_items = workgroups, a multiple of n_lists): workgroup w keeps list
-  // w % n_lists and appends the (key, index) pairs of every score whose first digit is at or
-  // above the lowest digit the k'-th key can still have (from the list's histogram as it fills)
-  // to its own region of the list's candidate buffer (hist + cand_off words; region w / n_lists of
-  // cand_region pairs, its pair count written at SELECT_RCOUNT_WORD + w / n_lists); `scores` may
-  // then be null (no dense scores written)
+  // scores_cand_chunk(), n_items = workgroups, a multiple of n_lists, cand_region >=
+  // scores_cand_region(s_stride, n_items / n_lists)): workgroup w keeps list w / nper (nper =
+  // n_items / n_lists), takes units of `chunk` tokens from the list's counter (SELECT_CLAIM_WORD) and
+  // appends the (key, index) pairs of every score whose first digit is at or above the lowest digit
+  // the k'-th key can still have (from the list's histogram as it fills) to its own region of the
+  // list's candidate buffer (hist + cand_off words; region w % nper of cand_region pairs, its pair
+  // count written at SELECT_RCOUNT_WORD + w % nper); `scores` may then be null (no dense scores)
   int64_t cand_off;
   int64_t cand_region;
   int top_k;
@@ -168,11 +169,15 @@ hipError_t launch_select(const SelectArgs& a, int n_lists, bool fused_prefix, hi
 hipError_t launch_select_blocks(const SelectArgs& a, int n_lists, int64_t max_cand, hipStream_t st);
 int64_t select_blocks_max_candidates();
 hipError_t launch_scores_wave(const ScoreArgs& a, int kvt, hipStream_t st);
-// candidate mode of scores_wave: tokens per item (ScoreArgs::chunk), items walked chunk-major
+// candidate mode of scores_wave: tokens per unit of work (ScoreArgs::chunk), units taken in order;
+// the region size (pairs) each of nper workgroups per list needs for a list of s_stride candidates
 int scores_cand_chunk();
+int64_t scores_cand_region(int64_t s_stride, int nper);
 constexpr int SELECT_ZERO_WORDS = 4100;   // per-list words the selection needs cleared
 constexpr int SELECT_CCOUNT_WORD = 4096;  // per-list word: candidate pairs appended so far
 constexpr int SELECT_RCOUNT_WORD = 2048;  // candidate mode: per-list pair counts of the regions (<= 256)
+constexpr int SELECT_CLAIM_WORD = 4099;   // candidate mode: per-list counter of the units taken
+static_assert(SELECT_CLAIM_WORD < SELECT_ZERO_WORDS && SELECT_CLAIM_WORD != SELECT_CCOUNT_WORD, "cleared, unshared");
 // candidate mode: the score pass appended the candidate pairs (ScoreArgs::cand_off); one workgroup
 // per list, lists of at most SELECT_CAND_MAX_N candidates (an LDS bitmap over them)
 constexpr int SELECT_CAND_MAX_N = 1 << 20;

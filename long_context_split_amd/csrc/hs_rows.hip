@@ -93,8 +93,8 @@ __global__ __launch_bounds__(64 * NRG) void attn_rows_kernel(AttnArgs a) {
       const int q = tid + (i >> 1) * NT;
       const int tok = 2 * (q / PPR) + (i & 1);
       const size_t off = (size_t)min(base + tok, c1 - 1) * rstride + (q % PPR) * 16;
-      rk[i] = *(const u32x4*)(kbase + off);
-      rv[i] = *(const u32x4*)(vbase + off);
+      rk[i] = load_stream(kbase + off);
+      rv[i] = load_stream(vbase + off);
     }
     if (FP8 && tid < TT) {
       const size_t r = ((size_t)rs + min(base + tid, c1 - 1)) * a.n_kv + g;
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(64 * NRG) void attn_rows_kernel(AttnArgs a) {
       if (lane == 0) { fmm[wave][0] = fx; fmm[wave][1] = fn; }
     }
     __syncthreads();
-    prefetch(min(base + TT, last));                               // past the end: the last tile again (cache hit)
+    prefetch(base < last ? base + TT : c1);                       // past the end: every row clamps to the last one
     float fmax_t = sl2, fmin_t = sl2;
     if (FP8) {
 #pragma unroll
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(64 * NRG) void attn_rows_scores_kernel(ScoreArgs a)
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int p = tid + i * NT;
-      rk[i] = *(const u32x4*)(kbase + (size_t)min(base + p / PPR, c1 - 1) * rstride + (p % PPR) * 16);
+      rk[i] = load_stream(kbase + (size_t)min(base + p / PPR, c1 - 1) * rstride + (p % PPR) * 16);
     }
     if (FP8 && tid < TT) sk = a.k_scale[((size_t)rs + min(base + tid, c1 - 1)) * a.n_kv + g];
   };
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(64 * NRG) void attn_rows_scores_kernel(ScoreArgs a)
     }
     if (tid < TT) ksc[tid] = FP8 ? sk * sl2 : sl2;                // logit factor of the token
     __syncthreads();
-    prefetch(min(base + TT, last));
+    prefetch(base < last ? base + TT : c1);
 
 #pragma unroll 1
     for (int st = 0; st < NSUB; ++st) {

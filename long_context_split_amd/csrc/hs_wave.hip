@@ -118,8 +118,8 @@ __global__ __launch_bounds__(64 * NW) void attn_wave_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < PPL; ++i) {
       const size_t off = (size_t)row_of(i) * rstride + ((lane + 64 * i) % PPR) * 16;
-      rk[i] = *(const u32x4*)(kbase + off);
-      rv[i] = *(const u32x4*)(vbase + off);
+      rk[i] = load_stream(kbase + off);
+      rv[i] = load_stream(vbase + off);
     }
     if (FP8) {
       sk = a.k_scale[((size_t)rs + srow) * a.n_kv + g];
@@ -324,13 +324,14 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
   __shared__ float s_lse2[32];
   __shared__ int s_kd;                                           // CAND: lowest first digit appended
   __shared__ uint32_t s_cc;                                      // CAND: pairs in this workgroup's region
+  __shared__ uint32_t s_claimed;                                 // CAND: units this workgroup has taken
   static_assert(!CAND || NQ == 1, "candidate mode: one query token");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int list, cidx, slot = 0, nper = 1;                            // lists own max(fold, ceil(ncand / chunk)) items
   if constexpr (CAND) {
-    list = (int)blockIdx.x % a.n_lists;
-    slot = (int)blockIdx.x / a.n_lists;
-    nper = (int)gridDim.x / a.n_lists;                           // workgroups per list
+    nper = (int)gridDim.x / a.n_lists;                           // workgroups per list, on consecutive XCDs
+    list = (int)blockIdx.x / nper;
+    slot = (int)blockIdx.x % nper;
     cidx = slot;
   } else {
     grid_item(a.seq_len, a.n_kv, a.n_lists, a.chunk, a.window, a.part_ml ? 1 : 0, a.uniform_items, blockIdx.x, list,
@@ -347,20 +348,23 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
   const char* kbase = (const char*)a.k + ((size_t)rs * a.n_kv + g) * SB;
   const size_t rstride = (size_t)a.n_kv * SB;
   const int ntiles = c1 > c0 ? (c1 - c0 + TT - 1) / TT : 0;
-  // This wave's tiles q = 0 .. nq - 1 by first token; positions from cend on are masked (a CAND tile
-  // never crosses its item, whose tiles wave and wave + NW are this wave's q = 2j and 2j + 1).
-  const int nitem_all = CAND ? (ncand + a.chunk - 1) / a.chunk : 0;
-  const int nq = CAND ? (slot < nitem_all ? 2 * ((nitem_all - 1 - slot) / nper + 1) : 0)
-                      : (wave < ntiles ? (ntiles - 1 - wave) / NW + 1 : 0);
+  // Dense mode: this wave's tiles q = 0 .. nq - 1 of the chunk.  Candidate mode: units of UT = 2 tiles,
+  // unit u = tiles u % 8 and u % 8 + 8 of the 16-tile item u / 8 (consecutive units read one item
+  // together; one wave reading two adjacent tiles instead was slower), each wave's first two units
+  // static (unit slot * NW + wave, then that plus nper * NW), the rest taken in order from the list's
+  // counter by whichever wave of the list's workgroups is free, so slower XCDs take fewer.  Positions
+  // from cend on are masked.
+  constexpr int UT = 2 * TT;
+  const int nq = CAND ? 0 : (wave < ntiles ? (ntiles - 1 - wave) / NW + 1 : 0);
+  const int nunits = CAND ? (ncand + 8 * UT - 1) / (8 * UT) * 8 : 0;
   const int cend = CAND ? ncand : c1;
-  auto tstart = [&](int q) -> int {
-    if constexpr (CAND) return (slot + (q >> 1) * nper) * a.chunk + (wave + NW * (q & 1)) * TT;
-    else return c0 + (wave + NW * q) * TT;
-  };
+  auto tstart = [&](int q) -> int { return c0 + (wave + NW * q) * TT; };
+  auto ustart = [&](int u, int h) -> int { return u < nunits ? (u >> 3) * (8 * UT) + ((u & 7) + 8 * h) * TT : cend; };
+  int uk = slot * NW + wave;                                     // CAND: the unit in hand
   char* const kt = ktile[wave];
   // Two tiles in flight per wave: buffers A and B alternate (named, so every wait is a static count).
-  // Loads are clamped to the wave's last tile instead of skipped, so no branch surrounds a load; the
-  // repeated tile at the end hits in cache.
+  // Loads past the wave's last tile are not skipped (no branch surrounds a load) but start at cend, so
+  // every position clamps to the list's last row: one row, read again.
   u32x4 kA[PPL], kB[PPL];
   float sA = 0.f, sB = 0.f;
   auto load = [&](u32x4 (&kr)[PPL], float& ks, int ts) {        // clamped rows: no branch, in bounds
@@ -368,13 +372,16 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
     for (int i = 0; i < PPL; ++i) {
       const int p = lane + 64 * i;
       const int pos = min(ts + p / PPR, cend - 1);
-      kr[i] = *(const u32x4*)(kbase + (size_t)pos * rstride + (p % PPR) * 16);
+      kr[i] = load_stream(kbase + (size_t)pos * rstride + (p % PPR) * 16);
     }
     if (FP8) ks = a.k_scale[((size_t)rs + min(ts + lane, cend - 1)) * a.n_kv + g];
   };
-  if (nq > 0) {                                                  // in flight during the prologue below
+  if (CAND) {                                                    // in flight during the prologue below
+    load(kA, sA, ustart(uk, 0));
+    load(kB, sB, ustart(uk, 1));
+  } else if (nq > 0) {
     load(kA, sA, tstart(0));
-    load(kB, sB, tstart(min(1, nq - 1)));
+    load(kB, sB, nq > 1 ? tstart(1) : cend);
   }
   if (a.part_ml) {
     // The full layer's merge, folded in (at most 64 chunks): every workgroup derives the LSE of all rows
@@ -405,7 +412,7 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
   uint32_t* ghist = a.hist + ((size_t)b * a.n_kv + g) * a.hist_stride;   // CAND: the list's (one query token)
   if (CAND && wave == 0) {
     const int d = need_cand ? lower_digit(ghist, (uint32_t)kk, lane) : 2048;
-    if (lane == 0) { s_kd = d; s_cc = 0u; }
+    if (lane == 0) { s_kd = d; s_cc = 0u; s_claimed = 2u * NW; }
   }
   uint2* const region = CAND ? (uint2*)(ghist + a.cand_off) + (size_t)slot * a.cand_region : nullptr;
   for (int p = tid; p < 32 * 16; p += NT) {
@@ -511,28 +518,58 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
       }
     }
   };
-  for (int q = 0; q < nq; q += 2) {
-    process(kA, sA, tstart(q));
-    load(kA, sA, tstart(min(q + 2, nq - 1)));                    // past the end: the last tile again (cache hit)
-    if (q + 1 >= nq) break;
-    process(kB, sB, tstart(q + 1));
-    // on this wave's turn, a fresh bound from the list's histogram (here, while kB's registers are
-    // free; the next load of kB waits for it)
-    if (need_cand && (q >> 1) % NW == wave) {
-      const int d = lower_digit(ghist, (uint32_t)kk, lane);
-      if (lane == 0) atomicMax(&s_kd, d);
+  // this wave's share of the histogram to the list's global one (read and clear: adds that other waves
+  // make meanwhile stay for a later move), only its bins at or above the current bound: the bound never
+  // falls, so lower bins cannot move it (they reach the global histogram at the end)
+  auto flush_share = [&]() {
+    constexpr int SHARE = 2048 / NW;
+    const int lo = max(wave * SHARE, *(volatile int*)&s_kd);
+    for (int i = lo + lane; i < (wave + 1) * SHARE; i += 64) {
+      const uint32_t v = atomicExch(&hist[0][i], 0u);
+      if (v) atomicAdd(ghist + i, v);
     }
-    load(kB, sB, tstart(min(q + 3, nq - 1)));
-    if (need_cand) {
-      // this wave's share of the histogram to the list's global one (read and clear: adds that other
-      // waves make meanwhile stay for a later move), only its bins at or above the current bound: the
-      // bound never falls, so lower bins cannot move it (they reach the global histogram at the end)
-      constexpr int SHARE = 2048 / NW;
-      const int lo = max(wave * SHARE, *(volatile int*)&s_kd);
-      for (int i = lo + lane; i < (wave + 1) * SHARE; i += 64) {
-        const uint32_t v = atomicExch(&hist[0][i], 0u);
-        if (v) atomicAdd(ghist + i, v);
+  };
+  if constexpr (CAND) {
+    // A workgroup takes at most cap units (its region holds cap * UT pairs); the caps of a list's
+    // workgroups add up to at least twice its units, so every unit is taken.
+    const uint32_t cap = (uint32_t)(a.cand_region / UT);
+    uint32_t* const ctr = ghist + SELECT_CLAIM_WORD;
+    // (atomicInc, not atomicAdd: the compiler turns a uniform-address add into a wave-wide one whose
+    // result it broadcasts at once, which would wait for every load in flight)
+    // The value is used as returned (no arithmetic next to the atomic, which would wait for it).
+    auto claim = [&]() -> uint32_t {                             // lane 0: the counter's value, or ~0
+      uint32_t r = ~0u;
+      if (lane == 0 && atomicAdd(&s_claimed, 1u) < cap) r = atomicInc(ctr, ~0u);
+      return r;
+    };
+    // The claim for the unit after next is issued before that unit's loads, so reading it waits for
+    // nothing issued later.
+    uint32_t rc = (uint32_t)((nper + slot) * NW + wave), roff = 0u;   // the second static unit
+    for (int k = 0; uk < nunits; ++k) {
+      process(kA, sA, ustart(uk, 0));
+      const uint32_t raw = __builtin_amdgcn_readfirstlane(rc);
+      const int un = raw == ~0u ? nunits : (int)min(raw + roff, (uint32_t)nunits);
+      rc = claim();
+      roff = 2u * nper * NW;                                     // counter value c is unit c + 2 nper NW
+      load(kA, sA, ustart(un, 0));
+      process(kB, sB, ustart(uk, 1));
+      // on this wave's turn, a fresh bound from the list's histogram (here, while kB's registers are
+      // free; the next load of kB waits for it)
+      if (need_cand && k % NW == wave) {
+        const int d = lower_digit(ghist, (uint32_t)kk, lane);
+        if (lane == 0) atomicMax(&s_kd, d);
       }
+      load(kB, sB, ustart(un, 1));
+      if (need_cand) flush_share();
+      uk = un;
+    }
+  } else {
+    for (int q = 0; q < nq; q += 2) {
+      process(kA, sA, tstart(q));
+      load(kA, sA, q + 2 < nq ? tstart(q + 2) : cend);
+      if (q + 1 >= nq) break;
+      process(kB, sB, tstart(q + 1));
+      load(kB, sB, q + 3 < nq ? tstart(q + 3) : cend);
     }
   }
   if (!do_hist) return;
@@ -570,11 +607,19 @@ static void launch_scores_wave_t(const ScoreArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((scores_wave_kernel<KVT, NW, NQ, false>), dim3(a.n_items), dim3(64 * NW), 0, st, a);
 }
 
-int scores_cand_chunk() { return 2 * 8 * 64; }
+int scores_cand_chunk() { return 2 * 64; }
+
+int64_t scores_cand_region(int64_t s_stride, int nper) {
+  constexpr int NW = 8;
+  const int64_t units = (s_stride + 8 * scores_cand_chunk() - 1) / (8 * scores_cand_chunk()) * 8;
+  const int64_t share = (units + nper - 1) / nper;
+  return std::max<int64_t>(2 * share, 2 * NW) * scores_cand_chunk();
+}
 
 hipError_t launch_scores_wave(const ScoreArgs& a, int kvt, hipStream_t st) {
   if (a.R > 32 || a.n_q > 4 || (kvt != KV_BF16 && kvt != KV_FP8)) return hipErrorInvalidValue;
-  if (a.cand_off > 0 && (a.n_q != 1 || !a.hist || a.chunk != scores_cand_chunk() || a.n_items % a.n_lists))
+  if (a.cand_off > 0 && (a.n_q != 1 || !a.hist || a.chunk != scores_cand_chunk() || a.n_items % a.n_lists ||
+                         a.cand_region < scores_cand_region(a.s_stride, a.n_items / a.n_lists)))
     return hipErrorInvalidValue;
   const int nq = a.n_q == 1 ? 1 : a.n_q == 2 ? 2 : 4;
   if (kvt == KV_BF16) {

@@ -142,19 +142,20 @@ def test_select_blocks_budgets_and_long_list():
     _check_blocks(x.reshape(1, 1, 1, -1), [L], 1, 1, 1024, 128)
 
 
-@pytest.mark.parametrize("n_q,H,L", [(1, 32, 40000), (1, 32, 1153), (1, 32, 300), (2, 16, 40000)])
-def test_candidate_selection_paths_agree(n_q, H, L, monkeypatch):
+@pytest.mark.parametrize("n_q,H,L,B", [(1, 32, 40000, 16), (1, 32, 1153, 16), (1, 32, 300, 16), (2, 16, 40000, 16),
+                                       (1, 32, 9000, 272)])
+def test_candidate_selection_paths_agree(n_q, H, L, B, monkeypatch):
     """The full layer's selection three ways: from the candidates the score pass appends (the
     default for one query token, equal lengths and at least 16 lists; no dense scores stored),
     the same with the dense scores requested, and the dense three-kernel radix select.  All give
     identical lists, and the one with scores equals the oracle's selection on those scores.
-    L = 1153 leaves most score workgroups without an item, L = 300 selects every candidate; the
-    last sequence has identical K rows, so every score ties and the lowest indices must win."""
+    L = 1153 leaves most score workgroups without work, L = 300 selects every candidate, 272 lists
+    get one score workgroup each (almost every unit is taken from the list's counter); the last
+    sequence has identical K rows, so every score ties and the lowest indices must win."""
     import synth
     from long_context_split_amd import hysparse as hs
-    banner(f"candidate vs dense selection n_q={n_q} H={H} L={L}")
+    banner(f"candidate vs dense selection n_q={n_q} H={H} L={L} B={B}")
     rng = np.random.default_rng(21 + n_q + L)
-    B = 16
     lens = [L] * B
     k = rng.standard_normal((B * L, 1, 128)).astype(np.float32)
     k[(B - 1) * L:] = k[(B - 1) * L]                              # identical rows: all scores tied
