@@ -232,7 +232,10 @@ hs_status plan_full(const hs_kv_cache* kv, const hs_attn_params* p, hs_dtype q_d
   int maxc = 0;
   for (int b = 0; b < ci.B; ++b) maxc = std::max(maxc, kv->h_seq_len[b] - std::min(p->window, kv->h_seq_len[b]));
   pl.s_stride = maxc;
-  pl.chunk_s = env_int("HS_SCORE_CHUNK", 0) > 0 ? (int)align_up((size_t)env_int("HS_SCORE_CHUNK", 0), 256) : pl.chunk;
+  // score pass chunk: the dense one, halved for the many-row kernel (its registers allow two
+  // workgroups per CU, which hide more of the latency between its MFMA and exp phases)
+  pl.chunk_s = env_int("HS_SCORE_CHUNK", 0) > 0 ? (int)align_up((size_t)env_int("HS_SCORE_CHUNK", 0), 256)
+               : pl.rows ? std::max(tt, (int)align_up((size_t)(pl.chunk / 2), (size_t)tt)) : pl.chunk;
   pl.max_chunks_s = (maxc + pl.chunk_s - 1) / pl.chunk_s;
 
   size_t off = 0;

@@ -175,8 +175,14 @@ __global__ __launch_bounds__(64 * NRG) void attn_rows_kernel(AttnArgs a) {
     // (m only has to stay at or above the logits, minus TAU; LSE = m + log2(l) is exact for any m),
     // and the logits themselves are formed inside exp2's argument as fma(s, f, -m).
     constexpr float TAU = 8.f;
-    auto tile = [&](int st, auto masked) {
-      constexpr bool MASK = decltype(masked)::value;
+    auto tile = [&](int st, bool MASK) {
+      s16x8 va[4][2];                                               // V^T operands, read ahead of the softmax
+#pragma unroll
+      for (int mt4 = 0; mt4 < 4; ++mt4) {
+        const int d = 32 * mt4 + (lane & 31);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) va[mt4][u] = *(const s16x8*)(vt + d * VROW + vt_quad<TT / 8>(d, 4 * st + 2 * u + (lane >> 5)));
+      }
       f32x16 s = {};
       {
         const char* kb = kt + (32 * st + (lane & 31)) * KROW + (lane >> 5) * 16;
@@ -237,27 +243,22 @@ __global__ __launch_bounds__(64 * NRG) void attn_rows_kernel(AttnArgs a) {
         }
 #pragma unroll
       for (int mt4 = 0; mt4 < 4; ++mt4) {
-        const int d = 32 * mt4 + (lane & 31);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const s16x8 va = *(const s16x8*)(vt + d * VROW + vt_quad<TT / 8>(d, 4 * st + 2 * u + (lane >> 5)));
-          acc[mt4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va),
+          acc[mt4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[mt4][u]),
                                                              __builtin_bit_cast(bf16x8, ph[u]), acc[mt4], 0, 0, 0);
           if (SPLIT)
-            acc[mt4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va),
+            acc[mt4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[mt4][u]),
                                                                __builtin_bit_cast(bf16x8, pl[u]), acc[mt4], 0, 0, 0);
         }
       }
     };
-    if (base + TT <= c1) {                                          // full super-tile: no masking
+    // one loop (a separate loop for the masked last super-tile kept a second copy of acc); only a
+    // sub-tile that reaches past c1 masks
 #pragma unroll 1
-      for (int st = 0; st < NSUB; ++st) tile(st, std::false_type{});
-    } else {
-#pragma unroll 1
-      for (int st = 0; st < NSUB; ++st) {
-        if (base + 32 * st >= c1) break;
-        tile(st, std::true_type{});
-      }
+    for (int st = 0; st < NSUB; ++st) {
+      if (base + 32 * st >= c1) break;
+      tile(st, base + 32 * st + 32 > c1);
     }
     __syncthreads();
   }
