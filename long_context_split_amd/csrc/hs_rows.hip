@@ -118,6 +118,13 @@ __global__ __launch_bounds__(64 * NRG) void attn_rows_kernel(AttnArgs a) {
   float m = -INFINITY, lsum = 0.f;
   f32x16 acc[4] = {};
   const float sl2 = a.scale_log2;
+  // V^T operand of (row block mt4, k-step u, sub-tile st) for this lane: row d = 32 mt4 + (l & 31),
+  // column quad q = 4 st + 2 u + (l >> 5), swizzled as vt_quad does; with b = bit 4 of the lane,
+  // q ^ (2 (d >> 4)) = 4 (st ^ (mt4 mod NSUB)) + 2 (u ^ b) + (l >> 5), so the address is one of two
+  // per-lane bases plus a constant
+  const int vlb = (lane >> 4) & 1;
+  const char* const vb0 = vt + (lane & 31) * VROW + 16 * ((lane >> 5) + 2 * vlb);
+  const char* const vb1 = vt + (lane & 31) * VROW + 16 * ((lane >> 5) + 2 * (1 - vlb));
 
   for (int base = c0; base < c1; base += TT) {
     // ---- registers -> LDS: K as [token][d], V transposed as [d][token'] (bf16)
@@ -178,11 +185,10 @@ __global__ __launch_bounds__(64 * NRG) void attn_rows_kernel(AttnArgs a) {
     auto tile = [&](int st, bool MASK) {
       s16x8 va[4][2];                                               // V^T operands, read ahead of the softmax
 #pragma unroll
-      for (int mt4 = 0; mt4 < 4; ++mt4) {
-        const int d = 32 * mt4 + (lane & 31);
+      for (int mt4 = 0; mt4 < 4; ++mt4)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) va[mt4][u] = *(const s16x8*)(vt + d * VROW + vt_quad<TT / 8>(d, 4 * st + 2 * u + (lane >> 5)));
-      }
+        for (int u = 0; u < 2; ++u)
+          va[mt4][u] = *(const s16x8*)((u ? vb1 : vb0) + mt4 * 32 * VROW + 64 * (st ^ (mt4 & (NSUB - 1))));
       f32x16 s = {};
       {
         const char* kb = kt + (32 * st + (lane & 31)) * KROW + (lane >> 5) * 16;
@@ -255,7 +261,7 @@ __global__ __launch_bounds__(64 * NRG) void attn_rows_kernel(AttnArgs a) {
     };
     // one loop (a separate loop for the masked last super-tile kept a second copy of acc); only a
     // sub-tile that reaches past c1 masks
-#pragma unroll 1
+#pragma unroll
     for (int st = 0; st < NSUB; ++st) {
       if (base + 32 * st >= c1) break;
       tile(st, base + 32 * st + 32 > c1);

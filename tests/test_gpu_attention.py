@@ -185,6 +185,30 @@ def test_gqa_multi_query_tokens_bf16():
         _check_seq(up, res, i, top_k=200, window=16)
 
 
+@pytest.mark.parametrize("kvtype,n_kv,H,n_q", [("bf16", 1, 32, 3), ("e4m3", 2, 32, 4), ("e4m3", 1, 64, 2),
+                                              ("bf16", 1, 32, 8), ("bf16", 2, 32, 6)])
+def test_many_row_kernels(kvtype, n_kv, H, n_q):
+    """The many-row kernels (more than 32 query rows per KV head) at each row-group count: R = 96
+    and 128 (4 groups, 128-token super-tiles), 64 (2 groups, 64-token super-tiles), 256 and 96
+    with 8 and 6 query tokens per workgroup (no fused histogram); G = 16, 32 and 64; bf16 and
+    E4M3 caches; lengths that end inside a super-tile."""
+    banner(f"many-row kv={kvtype} n_kv={n_kv} H={H} n_q={n_q}")
+    rng = np.random.default_rng(40 + H + n_q + n_kv)
+    lens = [5000, 777]
+    tot = sum(lens)
+    k = rng.standard_normal((tot, n_kv, 128)).astype(np.float32)
+    v = rng.standard_normal((tot, n_kv, 128)).astype(np.float32)
+    if kvtype == "bf16":
+        k, v = synth.bf16_bits(k), synth.bf16_bits(v)
+    q = synth.bf16_bits(rng.standard_normal((2, n_q, H, 128)).astype(np.float32))
+    case = dict(spec=dict(kv=kvtype, q="bf16"), lengths=np.array(lens), row_start=np.array([0, lens[0]]),
+                q_full=q, q_sparse=[q], k=k, v=v, needles=[[], []])
+    up = Uploaded(case)
+    res = _run_block(up, top_k=200, window=16)
+    for i in range(2):
+        _check_seq(up, res, i, top_k=200, window=16)
+
+
 def test_fp8_cache_h64_q4():
     """Config 3's shape (H=64, 4 query tokens, FP8 E4M3 with per-token scales,
     near-duplicate key clusters) at a 64K context."""
