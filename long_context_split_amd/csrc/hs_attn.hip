@@ -299,10 +299,13 @@ __global__ __launch_bounds__(64 * NWR * NWT) void attn_partial_kernel(AttnArgs a
 // (row, list), all chunks in one online pass; otherwise one workgroup per (row, list) whose wave w
 // combines chunks w, w + 4, ..., then wave 0 combines the four parts in a fixed order.  The first
 // partial loads do not wait for the list's count (merge_part_wave).
-template <bool ROWW>
-__global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
-  __shared__ float2 po[ROWW ? 1 : 4][64];
-  __shared__ float pm[4], pl[4];
+// ROWW: one wave per (row, list), four rows per workgroup (few chunks); otherwise one workgroup of
+// NWM waves per (row, list), wave w taking chunks w, w + NWM, ... (8 loads in flight per wave), the
+// waves' results combined through LDS in wave order.
+template <bool ROWW, int NWM>
+__global__ __launch_bounds__(64 * NWM) void attn_merge_kernel(MergeArgs a) {
+  __shared__ float2 po[ROWW ? 1 : NWM][64];
+  __shared__ float pm[NWM], pl[NWM];
   const int list = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = ROWW ? blockIdx.x * 4 + wave : blockIdx.x;
@@ -315,7 +318,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
   const int nch = min((ntok + a.chunk - 1) / a.chunk, a.max_chunks);
   const size_t first = (size_t)list * a.max_chunks * a.R + row;
   const MergePart r = merge_part_wave(a.part_ml + first * 2, (size_t)a.R * 2, a.part_acc + first * D, (size_t)a.R * D,
-                                      ROWW ? 0 : wave, nch, a.max_chunks, ROWW ? 1 : 4, lane);
+                                      ROWW ? 0 : wave, nch, a.max_chunks, ROWW ? 1 : NWM, lane);
   float mx, ls;
   float2 o;
   if constexpr (ROWW) {
@@ -325,12 +328,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
     if (lane == 0) { pm[wave] = r.m; pl[wave] = r.l; }
     __syncthreads();
     if (wave) return;
-    mx = fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3]));
+    mx = pm[0];
+#pragma unroll
+    for (int w = 1; w < NWM; ++w) mx = fmaxf(mx, pm[w]);
     const float msub = mx == -INFINITY ? 0.f : mx;
     ls = 0.f;
     o = make_float2(0.f, 0.f);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NWM; ++w) {
       const float wt = exp2f(pm[w] - msub);
       ls += wt * pl[w];
       o.x += wt * po[w][lane].x;
@@ -519,10 +524,13 @@ hipError_t launch_attn_partial(const AttnArgs& a, int kvt, int ct, int nwr, bool
 hipError_t launch_attn_merge(const MergeArgs& m, hipStream_t st) {
   if (m.max_chunks <= 16) {
     dim3 grid((m.R + 3) / 4, m.n_lists);
-    hipLaunchKernelGGL(attn_merge_kernel<true>, grid, dim3(256), 0, st, m);
-  } else {
+    hipLaunchKernelGGL((attn_merge_kernel<true, 4>), grid, dim3(256), 0, st, m);
+  } else if (m.max_chunks <= 64) {
     dim3 grid(m.R, m.n_lists);
-    hipLaunchKernelGGL(attn_merge_kernel<false>, grid, dim3(256), 0, st, m);
+    hipLaunchKernelGGL((attn_merge_kernel<false, 4>), grid, dim3(256), 0, st, m);
+  } else {                                                        // 2 rounds of 8 loads per wave at 256 chunks
+    dim3 grid(m.R, m.n_lists);
+    hipLaunchKernelGGL((attn_merge_kernel<false, 16>), grid, dim3(1024), 0, st, m);
   }
   return hipGetLastError();
 }
