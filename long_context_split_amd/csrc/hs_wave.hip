@@ -377,8 +377,10 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
     if (FP8) ks = a.k_scale[((size_t)rs + min(ts + lane, cend - 1)) * a.n_kv + g];
   };
   if (CAND) {                                                    // in flight during the prologue below
-    load(kA, sA, ustart(uk, 0));
-    load(kB, sB, ustart(uk, 1));
+    if (nunits > 0) {                                            // else no row to clamp to (L_b <= window)
+      load(kA, sA, ustart(uk, 0));
+      load(kB, sB, ustart(uk, 1));
+    }
   } else if (nq > 0) {
     load(kA, sA, tstart(0));
     load(kB, sB, nq > 1 ? tstart(1) : cend);

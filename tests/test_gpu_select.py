@@ -143,15 +143,16 @@ def test_select_blocks_budgets_and_long_list():
 
 
 @pytest.mark.parametrize("n_q,H,L,B", [(1, 32, 40000, 16), (1, 32, 1153, 16), (1, 32, 300, 16), (2, 16, 40000, 16),
-                                       (1, 32, 9000, 272)])
+                                       (1, 32, 9000, 272), (1, 32, 129, 16), (1, 32, 100, 16)])
 def test_candidate_selection_paths_agree(n_q, H, L, B, monkeypatch):
     """The full layer's selection three ways: from the candidates the score pass appends (the
     default for one query token, equal lengths and at least 16 lists; no dense scores stored),
     the same with the dense scores requested, and the dense three-kernel radix select.  All give
     identical lists, and the one with scores equals the oracle's selection on those scores.
     L = 1153 leaves most score workgroups without work, L = 300 selects every candidate, 272 lists
-    get one score workgroup each (almost every unit is taken from the list's counter); the last
-    sequence has identical K rows, so every score ties and the lowest indices must win."""
+    get one score workgroup each (almost every unit is taken from the list's counter), L = 129
+    leaves one candidate and L = 100 none (the window takes every row); the last sequence has
+    identical K rows, so every score ties and the lowest indices must win."""
     import synth
     from long_context_split_amd import hysparse as hs
     banner(f"candidate vs dense selection n_q={n_q} H={H} L={L} B={B}")
@@ -166,7 +167,7 @@ def test_candidate_selection_paths_agree(n_q, H, L, B, monkeypatch):
     qd = dev(q)
     _, _, idx_a, cnt_a = hs.full_attn_select(kv, qd)
     S = hs.scores_stride(kv, 128)
-    sc = torch.empty((B, n_q, 1, S), dtype=torch.float32, device="cuda")
+    sc = torch.empty((B, n_q, 1, max(S, 1)), dtype=torch.float32, device="cuda")
     _, _, idx_b, cnt_b = hs.full_attn_select(kv, qd, scores_out=sc)
     monkeypatch.setenv("HS_DENSE_SELECT", "1")
     _, _, idx_c, cnt_c = hs.full_attn_select(kv, qd)
