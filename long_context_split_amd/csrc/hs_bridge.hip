@@ -9,9 +9,11 @@
 // stored at cache rows row_offset + t, as bf16 (round to nearest even) or as
 // OCP E4M3FN codes with one float32 scale per row (scale = amax / 448).
 //
-// Workgroup tile: 128 tokens x 256 columns (one target: K's 128 columns, then
-// V's), K-stage 64, 4 waves each owning 64 rows x 128 columns = one head block,
-// so a row's amax is reduced inside one wave.  MFMA v_mfma_f32_32x32x16_bf16,
+// Workgroup tile: 256 tokens x 256 columns (one target: K's 128 columns, then
+// V's), K-stage 64, 8 waves each owning 64 rows x 128 columns = one head block,
+// so a row's amax is reduced inside one wave; one workgroup per CU.  The stages
+// are double-buffered in LDS (one barrier per stage) and the global loads run
+// two stages ahead in two register buffers.  MFMA v_mfma_f32_32x32x16_bf16,
 // operands from LDS as 16-byte reads: A = rows of X, B = rows of W^T.  W is
 // stored transposed ([column][k]) at stage time: each thread loads the same
 // 8-column piece of two adjacent k rows and writes 32-bit (k, k+1) pairs; the
@@ -25,25 +27,26 @@
 namespace hs {
 
 namespace {
-constexpr int BM = 128, BN = 256, BK = 64, NT = 256;
+constexpr int BM = 256, BN = 256, BK = 64, NT = 512;
 constexpr int AROW = BK * 2 + 16;               // 144 B per X row in LDS
 constexpr int BROW = BK * 2 + 16;               // 144 B per column of W^T in LDS
-constexpr int STAGE = BM * AROW + BN * BROW;    // 55296 B
-constexpr int EPI = 4 * 64 * 128 * 2;           // per-wave 64 x 128 bf16 staging
-constexpr int SMEM = STAGE > EPI ? STAGE : EPI;
+constexpr int STAGE = BM * AROW + BN * BROW;    // 73728 B
+constexpr int EPI = 8 * 64 * 128 * 2;           // per-wave 64 x 128 bf16 staging
+constexpr int SMEM = 2 * STAGE > EPI ? 2 * STAGE : EPI;
 constexpr int APT = BM * BK * 2 / 16 / NT;      // X pieces per thread per stage (4)
-constexpr int BPT = BK * BN * 2 / 16 / NT;      // W pieces per thread per stage (8)
+constexpr int BPT = BK * BN * 2 / 16 / NT;      // W pieces per thread per stage (4: two k-row pairs)
+static_assert(APT == 4 && BPT == 4, "load split");
 
 __device__ __forceinline__ int crow(int lane, int r) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
 // byte offset of k-quad qd (8 k values) of W^T column n: quads XOR-swizzled per 8-column group
 __device__ __forceinline__ int wt_off(int n, int qd) { return n * BROW + 16 * (qd ^ ((n >> 3) & 7)); }
+
+struct Regs { u32x4 a[APT], b[BPT]; };
 }  // namespace
 
-__global__ __launch_bounds__(NT, 2) void bridge_kernel(BridgeArgs a) {
+__global__ __launch_bounds__(NT) void bridge_kernel(BridgeArgs a) {
   __shared__ __align__(16) char smem[SMEM];
-  char* const As = smem;
-  char* const Bs = smem + BM * AROW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t m0 = (int64_t)blockIdx.x * BM;
@@ -51,47 +54,47 @@ __global__ __launch_bounds__(NT, 2) void bridge_kernel(BridgeArgs a) {
   const uint16_t* wk = a.w[2 * tgt];
   const uint16_t* wv = a.w[2 * tgt + 1];
   const int Dm = a.Dm;
+  const int S = Dm / BK;                                          // stages (>= 1)
 
-  u32x4 ra[APT], rb[BPT];
-  auto load = [&](int k0) {
+  auto load = [&](Regs& r, int s) {                               // stage s; past the last: stage S - 1 again
+    const int k0 = min(s, S - 1) * BK;
 #pragma unroll
     for (int i = 0; i < APT; ++i) {
       const int p = tid + NT * i, row = p >> 3, c = p & 7;
-      const int64_t gr = m0 + row;
-      ra[i] = gr < a.T ? *(const u32x4*)(a.x + gr * Dm + k0 + c * 8) : u32x4{0u, 0u, 0u, 0u};
+      const int64_t gr = min(m0 + row, a.T - 1);                  // rows past T are never stored
+      r.a[i] = *(const u32x4*)(a.x + gr * Dm + k0 + c * 8);
     }
 #pragma unroll
     for (int i = 0; i < BPT; ++i) {                               // pair i/2: k rows 2 kp, 2 kp + 1
       const int q = tid + NT * (i >> 1), kp = q >> 5, np = q & 31;
       const uint16_t* src = (np < 16 ? wk : wv) + (int64_t)(k0 + 2 * kp + (i & 1)) * D + (np & 15) * 8;
-      rb[i] = *(const u32x4*)src;
+      r.b[i] = *(const u32x4*)src;
     }
   };
-  auto store = [&]() {
+  auto store = [&](const Regs& r, int buf) {
+    char* const As = smem + buf * STAGE;
+    char* const Bs = As + BM * AROW;
 #pragma unroll
     for (int i = 0; i < APT; ++i) {
       const int p = tid + NT * i;
-      *(u32x4*)(As + (p >> 3) * AROW + (p & 7) * 16) = ra[i];
+      *(u32x4*)(As + (p >> 3) * AROW + (p & 7) * 16) = r.a[i];
     }
 #pragma unroll
     for (int jp = 0; jp < BPT / 2; ++jp) {                        // W^T: word (k, k + 1) of column n
       const int q = tid + NT * jp, kp = q >> 5, np = q & 31;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t a0 = rb[2 * jp][e >> 1], a1 = rb[2 * jp + 1][e >> 1];
+        const uint32_t a0 = r.b[2 * jp][e >> 1], a1 = r.b[2 * jp + 1][e >> 1];
         const uint32_t word = (e & 1) ? ((a0 >> 16) | (a1 & 0xFFFF0000u)) : ((a0 & 0xFFFFu) | (a1 << 16));
         const int n = 8 * np + e;
         *(uint32_t*)(Bs + wt_off(n, kp >> 2) + 4 * (kp & 3)) = word;
       }
     }
   };
-
   f32x16 acc[2][4] = {};
-  load(0);
-  for (int k0 = 0; k0 < Dm; k0 += BK) {
-    store();
-    __syncthreads();
-    if (k0 + BK < Dm) load(k0 + BK);
+  auto compute = [&](int buf) {
+    const char* const As = smem + buf * STAGE;
+    const char* const Bs = As + BM * AROW;
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
       s16x8 av[2], bv[4];
@@ -110,6 +113,29 @@ __global__ __launch_bounds__(NT, 2) void bridge_kernel(BridgeArgs a) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[i]),
                                                                __builtin_bit_cast(bf16x8, bv[j]), acc[i][j], 0, 0, 0);
     }
+  };
+
+  // Stage s is computed from LDS buffer s % 2.  Iteration s stores stage s + 1 (loaded two
+  // iterations earlier) into the other buffer, loads stage s + 3 into the registers it just
+  // emptied, computes stage s, and ends with the one barrier of the stage.  Register buffers R0 / R1
+  // alternate (the loop handles two stages per pass, so each wait is a static count); loads past the
+  // last stage re-read it; storing them (unconditionally: a branch around the store would make the
+  // compiler wait for every load in flight) writes a buffer no later stage reads.
+  Regs r0, r1;
+  load(r0, 0);
+  load(r1, 1);
+  store(r0, 0);
+  load(r0, 2);
+  __syncthreads();
+  for (int s = 0; s < S; s += 2) {
+    store(r1, 1);
+    load(r1, s + 3);
+    compute(0);
+    __syncthreads();
+    if (s + 1 >= S) break;
+    store(r0, 0);
+    load(r0, s + 4);
+    compute(1);
     __syncthreads();
   }
 
