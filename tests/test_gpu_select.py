@@ -143,7 +143,8 @@ def test_select_blocks_budgets_and_long_list():
 
 
 @pytest.mark.parametrize("n_q,H,L,B", [(1, 32, 40000, 16), (1, 32, 1153, 16), (1, 32, 300, 16), (2, 16, 40000, 16),
-                                       (1, 32, 9000, 272), (1, 32, 129, 16), (1, 32, 100, 16)])
+                                       (1, 32, 9000, 272), (1, 32, 129, 16), (1, 32, 100, 16), (1, 32, 20000, 20),
+                                       (1, 32, 20000, 40)])
 def test_candidate_selection_paths_agree(n_q, H, L, B, monkeypatch):
     """The full layer's selection three ways: from the candidates the score pass appends (the
     default for one query token, equal lengths and at least 16 lists; no dense scores stored),
@@ -151,8 +152,9 @@ def test_candidate_selection_paths_agree(n_q, H, L, B, monkeypatch):
     identical lists, and the one with scores equals the oracle's selection on those scores.
     L = 1153 leaves most score workgroups without work, L = 300 selects every candidate, 272 lists
     get one score workgroup each (almost every unit is taken from the list's counter), L = 129
-    leaves one candidate and L = 100 none (the window takes every row); the last sequence has
-    identical K rows, so every score ties and the lowest indices must win."""
+    leaves one candidate and L = 100 none (the window takes every row), 20 and 40 lists get 12 and 6
+    score workgroups each (not aligned with the 8 XCDs); the last sequence has identical K rows, so
+    every score ties and the lowest indices must win."""
     import synth
     from long_context_split_amd import hysparse as hs
     banner(f"candidate vs dense selection n_q={n_q} H={H} L={L} B={B}")
