@@ -444,7 +444,19 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
   }
   const int tpw = a.G >= 32 ? 1 : 32 / a.G;                      // query tokens in the 32 rows
   float* sout = a.scores ? a.scores + (size_t)b * a.n_q * a.n_kv * a.s_stride : nullptr;
-  auto process = [&](const u32x4 (&kr)[PPL], float ks, int ts) {
+  // (key, index) of a score to the workgroup's region when its first digit reaches the bound; whole wave
+  auto append = [&](uint32_t key, int pos) {
+    const bool keep = lane < 32 && pos < cend && cand_digit(key) >= *(volatile int*)&s_kd;
+    const unsigned long long mk = __ballot(keep);
+    if (mk) {
+      uint32_t base = 0u;
+      if (lane == 0) base = atomicAdd(&s_cc, (uint32_t)__popcll(mk));
+      base = __shfl(base, 0);
+      if (keep) region[base + __popcll(mk & ((1ull << lane) - 1ull))] = make_uint2(key, (uint32_t)pos);
+    }
+  };
+  // hold != null: the keys are kept (hold[half]) instead of appended
+  auto process = [&](const u32x4 (&kr)[PPL], float ks, int ts, uint32_t* hold) {
     wave_sync();
 #pragma unroll
     for (int i = 0; i < PPL; ++i) {                              // registers -> LDS (FP8 -> bf16)
@@ -507,16 +519,9 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
           if (do_hist) atomicAdd(&hist[t][CAND ? cand_digit(f32_key(tv[t])) : (int)(f32_key(tv[t]) >> 21)], 1u);
         }
       }
-      if (need_cand) {                                           // append (key, index) to the workgroup's region
-        const uint32_t key = f32_key(tv[0]);
-        const bool keep = lane < 32 && pos < cend && cand_digit(key) >= *(volatile int*)&s_kd;
-        const unsigned long long mk = __ballot(keep);
-        if (mk) {
-          uint32_t base = 0u;
-          if (lane == 0) base = atomicAdd(&s_cc, (uint32_t)__popcll(mk));
-          base = __shfl(base, 0);
-          if (keep) region[base + __popcll(mk & ((1ull << lane) - 1ull))] = make_uint2(key, (uint32_t)pos);
-        }
+      if (need_cand) {
+        if (hold) hold[half] = f32_key(tv[0]);
+        else append(f32_key(tv[0]), pos);
       }
     }
   };
@@ -547,14 +552,36 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
     // The claim for the unit after next is issued before that unit's loads, so reading it waits for
     // nothing issued later.
     uint32_t rc = (uint32_t)((nper + slot) * NW + wave), roff = 0u;   // the second static unit
-    for (int k = 0; uk < nunits; ++k) {
-      process(kA, sA, ustart(uk, 0));
+    // The first unit's keys are held until the list's histogram has the first units' counts: after
+    // them every wave refreshes the bound, then appends the held keys that reach it (most of the
+    // first units' scores would otherwise be appended before any bound exists).
+    if (uk < nunits) {
+      uint32_t hk[4];
+      process(kA, sA, ustart(uk, 0), hk);
+      const uint32_t raw = __builtin_amdgcn_readfirstlane(rc);
+      const int un = (int)min(raw, (uint32_t)nunits);
+      rc = claim();
+      roff = 2u * nper * NW;
+      load(kA, sA, ustart(un, 0));
+      process(kB, sB, ustart(uk, 1), hk + 2);
+      load(kB, sB, ustart(un, 1));
+      if (need_cand) {
+        flush_share();
+        const int d = lower_digit(ghist, (uint32_t)kk, lane);
+        if (lane == 0) atomicMax(&s_kd, d);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) append(hk[q], ustart(uk, q >> 1) + 32 * (q & 1) + (lane & 31));
+      }
+      uk = un;
+    }
+    for (int k = 1; uk < nunits; ++k) {
+      process(kA, sA, ustart(uk, 0), nullptr);
       const uint32_t raw = __builtin_amdgcn_readfirstlane(rc);
       const int un = raw == ~0u ? nunits : (int)min(raw + roff, (uint32_t)nunits);
       rc = claim();
       roff = 2u * nper * NW;                                     // counter value c is unit c + 2 nper NW
       load(kA, sA, ustart(un, 0));
-      process(kB, sB, ustart(uk, 1));
+      process(kB, sB, ustart(uk, 1), nullptr);
       // on this wave's turn, a fresh bound from the list's histogram (here, while kB's registers are
       // free; the next load of kB waits for it)
       if (need_cand && k % NW == wave) {
@@ -567,10 +594,10 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
     }
   } else {
     for (int q = 0; q < nq; q += 2) {
-      process(kA, sA, tstart(q));
+      process(kA, sA, tstart(q), nullptr);
       load(kA, sA, q + 2 < nq ? tstart(q + 2) : cend);
       if (q + 1 >= nq) break;
-      process(kB, sB, tstart(q + 1));
+      process(kB, sB, tstart(q + 1), nullptr);
       load(kB, sB, q + 3 < nq ? tstart(q + 3) : cend);
     }
   }
