@@ -9,9 +9,11 @@
 // A decode step has few tokens (one per sequence), so the product is GEMV-
 // shaped: the weights (n_targets x 2 x d_model x 128 bf16, 8 MB for 4 targets
 // at d_model 4096) dominate the bytes.  Two kernels:
-//   append_partial  split-K over d_model: workgroup (k slice of 256, head block)
-//                   stages its weight slice transposed ([column][k]) and the
-//                   tokens' x slice in LDS and multiplies them with
+//   append_partial  split-K over d_model: workgroup (k slice of 128, head block)
+//                   stages its weight slice transposed ([column][k]; each
+//                   thread transposes one 8 x 8 block in registers and writes
+//                   8 columns of 8 k values) and the tokens' x slice in LDS
+//                   and multiplies them with
 //                   v_mfma_f32_32x32x16_bf16 (32 tokens x 32 columns per wave);
 //                   float32 partial sums to the workspace.
 //   append_finish   one wave per (token, head block): sums the slices in a
@@ -27,9 +29,13 @@ namespace hs {
 
 namespace {
 
-constexpr int KSL = 256;                  // d_model slice per workgroup
+constexpr int KSL = 128;                  // d_model slice per workgroup
 constexpr int PITCH = KSL * 2 + 16;       // LDS row pitch (bytes) of the staged slices
 constexpr int NTOK = 32;                  // tokens per M tile
+
+// byte offset of 8-k quad q of W^T column c: the quads are XOR-swizzled by the column's group of 8,
+// which spreads the block-transposing writes (16 column groups, one quad) over the LDS banks
+__device__ __forceinline__ int wq_off(int c, int q) { return c * PITCH + 16 * (q ^ ((c >> 3) & 15)); }
 
 }  // namespace
 
@@ -42,14 +48,27 @@ __global__ __launch_bounds__(256) void append_partial_kernel(AppendArgs a) {
   const int k0 = ks * KSL;
   const int kn = min(KSL, a.Dm - k0);                             // a multiple of 64
   const uint16_t* w = a.w[hb] + (size_t)k0 * 128;
-  // W slice: kn rows of 128 bf16; piece = 8 columns of one k row
-  for (int p = tid; p < KSL * 16; p += 256) {
-    const int k = p >> 4, c8 = (p & 15) * 8;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (k < kn) v = *(const u32x4*)(w + (size_t)k * 128 + c8);
+  // W slice (kn rows of 128 bf16): thread (kg, cg) takes the 8 x 8 block of k rows 8 kg .. and
+  // columns 8 cg .., rows past kn read as zero (clamped loads, no branch around them)
+  {
+    const int kg = tid >> 4, cg = tid & 15;
+    u32x4 r[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      *(uint16_t*)(wt + (c8 + j) * PITCH + k * 2) = (uint16_t)(v[j >> 1] >> (16 * (j & 1)));
+    for (int i = 0; i < 8; ++i) {
+      const int k = 8 * kg + i;
+      r[i] = *(const u32x4*)(w + (size_t)min(k, kn - 1) * 128 + 8 * cg);
+      if (k >= kn) r[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {                                 // column 8 cg + e: words (k, k + 1)
+      u32x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t a0 = r[2 * j][e >> 1], a1 = r[2 * j + 1][e >> 1];
+        o[j] = (e & 1) ? ((a0 >> 16) | (a1 & 0xFFFF0000u)) : ((a0 & 0xFFFFu) | (a1 << 16));
+      }
+      *(u32x4*)(wt + wq_off(8 * cg + e, kg)) = o;
+    }
   }
   // x slice: NTOK tokens of this M tile (rows past n_tokens are zero)
   for (int p = tid; p < NTOK * (KSL / 8); p += 256) {
@@ -63,9 +82,9 @@ __global__ __launch_bounds__(256) void append_partial_kernel(AppendArgs a) {
   // C[token][column] for columns 32 wave .. + 31: A = x rows, B = W^T rows (both k-contiguous)
   f32x16 c = {};
   const char* ab = xs + (lane & 31) * PITCH + (lane >> 5) * 16;
-  const char* bb = wt + (32 * wave + (lane & 31)) * PITCH + (lane >> 5) * 16;
+  const int bcol = 32 * wave + (lane & 31);
   for (int s = 0; s < kn / 16; ++s) {
-    const s16x8 av = *(const s16x8*)(ab + 32 * s), bv = *(const s16x8*)(bb + 32 * s);
+    const s16x8 av = *(const s16x8*)(ab + 32 * s), bv = *(const s16x8*)(wt + wq_off(bcol, 2 * s + (lane >> 5)));
     c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), c, 0, 0, 0);
   }
   // partial [slice][block][m tile][token][128] float32: lane holds column (l & 31), tokens crow(lane, r)
