@@ -388,21 +388,47 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
   if (a.part_ml) {
     // The full layer's merge, folded in (at most 64 chunks): every workgroup derives the LSE of all rows
     // from the chunk partials; row r's output is merged by workgroup r % nwg of the list's nwg >= 1.
-    const int nchd = (Lb + a.dchunk - 1) / a.dchunk;
+    const int nchd = (Lb + a.dchunk - 1) / a.dchunk;             // <= 64: one chunk per lane
     const int nwg = CAND ? nper : max(1, (ncand + a.chunk - 1) / a.chunk);
     if (cidx >= nwg) return;
     const size_t first = (size_t)list * a.dmax_chunks * a.R;
-    for (int r = wave; r < a.R; r += NW) {
-      const float* ml = a.part_ml + (first + r) * 2;
-      const float l2 = merged_lse2(ml, (size_t)a.R * 2, nchd, lane);
-      if (lane == 0) s_lse2[r] = l2;
-      if (r % nwg != cidx) continue;
-      const float2 o = l2 == -INFINITY ? make_float2(0.f, 0.f)
-                                       : merged_o(ml, (size_t)a.R * 2, a.part_acc + (first + r) * D, (size_t)a.R * D,
-                                                  0, nchd, 1, l2, lane);
-      const size_t orow = ((size_t)b * a.n_q + r / a.G) * a.H + (size_t)g * a.G + r % a.G;
+    // Rows wave + NW i (i < RPW) for the LSE table, and the rows this wave merges: the workgroup's rows
+    // (r % nwg == cidx) taken in turn by its waves, mr_j = cidx + nwg (wave + NW j) < R.  Their chunk
+    // partials are loaded in one batch (lane = chunk), then reduced row by row.
+    constexpr int RPW = (32 + NW - 1) / NW;                      // rows per wave (R <= 32)
+    auto mrow = [&](int j) { return cidx + nwg * (wave + NW * j); };
+    float2 v[2 * RPW];
+#pragma unroll
+    for (int i = 0; i < 2 * RPW; ++i) {
+      const int r = min(i < RPW ? wave + NW * i : mrow(i - RPW), a.R - 1);
+      v[i] = *(const float2*)(a.part_ml + ((first + r) + (size_t)min(lane, nchd - 1) * a.R) * 2);
+      if (lane >= nchd) v[i] = make_float2(-INFINITY, 0.f);
+    }
+    float l2m[RPW];
+#pragma unroll
+    for (int i = 0; i < 2 * RPW; ++i) {
+      const int r = i < RPW ? wave + NW * i : mrow(i - RPW);
+      if (r >= a.R) continue;                                    // uniform over the wave
+      const float mx = wave_max(v[i].x);
+      const float ls = mx == -INFINITY ? 0.f : wave_sum(exp2f(v[i].x - mx) * v[i].y);
+      const float l2 = ls > 0.f ? mx + __log2f(ls) : -INFINITY;
+      if (i < RPW) {
+        if (lane == 0) s_lse2[r] = l2;
+      } else {
+        l2m[i - RPW] = l2;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const int mr = mrow(j);
+      if (mr >= a.R) break;
+      const float* ml = a.part_ml + (first + mr) * 2;
+      const float2 o = l2m[j] == -INFINITY ? make_float2(0.f, 0.f)
+                                           : merged_o(ml, (size_t)a.R * 2, a.part_acc + (first + mr) * D,
+                                                      (size_t)a.R * D, 0, nchd, 1, l2m[j], lane);
+      const size_t orow = ((size_t)b * a.n_q + mr / a.G) * a.H + (size_t)g * a.G + mr % a.G;
       *(float2*)(a.out + orow * D + 2 * lane) = o;
-      if (lane == 0 && a.lse) a.lse[orow] = l2 * LN2;
+      if (lane == 0 && a.lse) a.lse[orow] = l2m[j] * LN2;
     }
   }
   if (!CAND && c0 >= ncand) return;
