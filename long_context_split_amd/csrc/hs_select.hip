@@ -374,6 +374,11 @@ __global__ __launch_bounds__(FIN_NT) void sel_cand_select_kernel(SelectArgs a) {
   const uint32_t* w = ws_list(a, list);
   const uint2* cand = (const uint2*)(w + a.cand_off);
   const int nreg = a.cand_regions;                                // <= 256
+  // the first-digit histogram is loaded first (it does not depend on the region counts) and searched
+  // in LDS, so neither the counts nor the search wait for it
+  uint32_t h1[2048 / FIN_NT];
+#pragma unroll
+  for (int i = 0; i < 2048 / FIN_NT; ++i) h1[i] = w[W_HIST1 + i * FIN_NT + tid];
   if (tid == 0) s_maxc = 1u;
   __syncthreads();
   if (tid < nreg) {
@@ -419,11 +424,6 @@ __global__ __launch_bounds__(FIN_NT) void sel_cand_select_kernel(SelectArgs a) {
         if ((v1 >> u) & 1u) f(c1[u].x, c1[u].y);
     }
   };
-  // the first-digit histogram is loaded ahead of the candidates and searched in LDS, so the search
-  // does not wait for them
-  uint32_t h1[2048 / FIN_NT];
-#pragma unroll
-  for (int i = 0; i < 2048 / FIN_NT; ++i) h1[i] = w[W_HIST1 + i * FIN_NT + tid];
   cload(c0, v0, 0);                                               // in flight during the first digit
   if (resident && npos > BATCH) cload(c1, v1, BATCH);
 #pragma unroll
