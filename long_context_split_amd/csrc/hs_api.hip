@@ -161,10 +161,10 @@ struct FullPlan {
   int ct, nwr, G, R, n_lists, chunk, max_chunks;
   int nwr_s, chunk_s, max_chunks_s;
   int64_t s_stride;
-  // candidate mode (one query token, equal lengths, wave path): score workgroups (about one per
-  // CU, a multiple of the lists), each filling its own region of cand_region pairs
-  int cand, cand_wgs;
-  int64_t cand_region;
+  // candidate mode (one query token, wave path): score workgroups (about one per CU; per list
+  // hs::cand_nper of its candidate count), each filling its own region of cand_region pairs
+  int cand, cand_wgs, cand_uniform;
+  int64_t cand_region, cand_total;
   size_t off_acc, off_ml, off_lse2, off_scores, off_sel, total;
   hs::SelectPlan sel;
 };
@@ -249,18 +249,33 @@ hs_status plan_full(const hs_kv_cache* kv, const hs_attn_params* p, hs_dtype q_d
   off += align_up((size_t)ci.B * p->q_tokens * ci.n_kv * pl.s_stride * 4, 256);
   bool equal_len = true;
   for (int b = 1; b < ci.B; ++b) equal_len = equal_len && kv->h_seq_len[b] == kv->h_seq_len[0];
-  // At least 16 lists: a list's score workgroups (256 / lists) store their first items unfiltered,
-  // which with fewer lists outweighs what candidate mode saves.
-  pl.cand = pl.wave && p->q_tokens == 1 && equal_len && p->select_block == 0 && pl.n_lists >= 16 &&
-            pl.s_stride <= hs::SELECT_CAND_MAX_N && !env_int("HS_DENSE_SELECT", 0);
+  // At least 16 lists (HS_CAND_MIN_LISTS): with fewer, each list has more score workgroups, which
+  // contend on its counter and histogram (ragged, 8 lists: 246 us against 241 with the dense
+  // selection; 16 lists: 392 against 403; 32: 707 against 737).  Ragged lengths: at most 64 lists
+  // (each score workgroup finds its list by a prefix over them).
+  const int cand_min_lists = env_int("HS_CAND_MIN_LISTS", 16);
+  pl.cand = pl.wave && p->q_tokens == 1 && p->select_block == 0 && pl.n_lists >= cand_min_lists &&
+            (equal_len || pl.n_lists <= 64) && pl.s_stride <= hs::SELECT_CAND_MAX_N &&
+            !env_int("HS_DENSE_SELECT", 0);
   pl.cand_wgs = 0;
   pl.cand_region = 0;
+  pl.cand_uniform = equal_len;
+  pl.cand_total = 0;
   int64_t cand_pairs = 0;
   if (pl.cand) {
-    const int nper = std::max(1, 256 / pl.n_lists);               // score workgroups per list
-    pl.cand_wgs = pl.n_lists * nper;
-    pl.cand_region = hs::scores_cand_region(pl.s_stride, nper);
-    cand_pairs = pl.cand_region * nper;
+    for (int l = 0; l < pl.n_lists; ++l) {
+      const int64_t L = kv->h_seq_len[l / ci.n_kv];
+      pl.cand_total += L - std::min<int64_t>(p->window, L);
+    }
+    int max_nper = 0;
+    for (int l = 0; l < pl.n_lists; ++l) {
+      const int64_t L = kv->h_seq_len[l / ci.n_kv], nc = L - std::min<int64_t>(p->window, L);
+      const int np = hs::cand_nper(nc, pl.cand_total);
+      pl.cand_wgs += np;
+      max_nper = std::max(max_nper, np);
+      pl.cand_region = std::max(pl.cand_region, hs::scores_cand_region(nc, np));
+    }
+    cand_pairs = pl.cand_region * max_nper;
   }
   hs::select_plan(pl.s_stride, pl.sel, cand_pairs);
   pl.off_sel = off;
@@ -522,6 +537,8 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
         sa.scores = scores_out;                                   // nullable: the test hook only
         sa.cand_off = pl.sel.cand_off;
         sa.cand_region = pl.cand_region;
+        sa.cand_uniform = pl.cand_uniform;
+        sa.cand_total = pl.cand_total;
         sa.top_k = p->top_k;
         sa.chunk = hs::scores_cand_chunk();
         sa.n_items = pl.cand_wgs;
@@ -541,7 +558,7 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
   se.sel_idx = sel_idx; se.sel_count = sel_count;
   se.ws = (uint32_t*)(ws + pl.off_sel); se.ws_stride = pl.sel.ws_stride; se.cand_off = pl.sel.cand_off;
   se.chunk = pl.sel.chunk; se.max_chunks = pl.sel.max_chunks;
-  se.cand_regions = pl.cand ? pl.cand_wgs / pl.n_lists : 0; se.cand_region = pl.cand_region;
+  se.cand_region = pl.cand_region;                               // region count per list: from the score pass
   if (p->select_block == 64)
     e = timed("select_blocks", s, [&] { return hs::launch_select_blocks(se, n_sel_lists, pl.s_stride, s); });
   else if (cand_mode)

@@ -78,16 +78,20 @@ struct ScoreArgs {
   float* out;
   float* lse;            // nullable, natural log
   // scores_wave, candidate mode (cand_off > 0; one query token, hist set, chunk =
-  // scores_cand_chunk(), n_items = workgroups, a multiple of n_lists, cand_region >=
-  // scores_cand_region(s_stride, n_items / n_lists)): workgroup w keeps list w / nper (nper =
-  // n_items / n_lists), takes units of `chunk` tokens from the list's counter (SELECT_CLAIM_WORD) and
-  // appends the (key, index) pairs of every score whose first digit is at or above the lowest digit
-  // the k'-th key can still have (from the list's histogram as it fills) to its own region of the
-  // list's candidate buffer (hist + cand_off words; region w % nper of cand_region pairs, its pair
-  // count written at SELECT_RCOUNT_WORD + w % nper); `scores` may then be null (no dense scores)
+  // scores_cand_chunk()): list l has cand_nper(ncand_l, cand_total) workgroups, consecutive in the
+  // grid (n_items = their sum; cand_uniform: every list has n_items / n_lists, found by division
+  // instead of a scan), cand_region >= scores_cand_region(ncand_l, nper_l) for every list.  A
+  // workgroup takes units of `chunk` tokens from its list's counter (SELECT_CLAIM_WORD) and appends
+  // the (key, index) pairs of every score whose first digit is at or above the lowest digit the k'-th
+  // key can still have (from the list's histogram as it fills) to its own region of the list's
+  // candidate buffer (hist + cand_off words; region `slot` of cand_region pairs, its pair count
+  // written at SELECT_RCOUNT_WORD + slot, the list's region count at SELECT_NREG_WORD); `scores`
+  // may then be null (no dense scores)
   int64_t cand_off;
   int64_t cand_region;
   int top_k;
+  int cand_uniform;
+  int64_t cand_total;    // sum over the lists of their candidate counts
 };
 
 struct SelectArgs {
@@ -100,8 +104,7 @@ struct SelectArgs {
   uint32_t* ws;          // [lists][ws_stride] words (layout in hs_select.hip)
   int64_t ws_stride, cand_off;
   int chunk, max_chunks; // candidates per chunk workgroup, chunks per list
-  int cand_regions;      // candidate mode: regions of cand_region pairs per list (one per score workgroup),
-  int64_t cand_region;   //   their pair counts at SELECT_RCOUNT_WORD
+  int64_t cand_region;   // candidate mode: region stride (pairs); the region count per list is at SELECT_NREG_WORD
 };
 
 struct SelectPlan {
@@ -177,6 +180,14 @@ constexpr int SELECT_ZERO_WORDS = 4100;   // per-list words the selection needs 
 constexpr int SELECT_CCOUNT_WORD = 4096;  // per-list word: candidate pairs appended so far
 constexpr int SELECT_RCOUNT_WORD = 2048;  // candidate mode: per-list pair counts of the regions (<= 256)
 constexpr int SELECT_CLAIM_WORD = 4099;   // candidate mode: per-list counter of the units taken
+constexpr int SELECT_NREG_WORD = 2304;    // candidate mode: per-list number of regions (score workgroups)
+static_assert(SELECT_NREG_WORD >= SELECT_RCOUNT_WORD + 256 && SELECT_NREG_WORD < SELECT_CCOUNT_WORD, "free word");
+// candidate mode: score workgroups of a list with ncand candidates out of `total` over all lists
+// (about 256 workgroups in all, at least one per list); the host and the kernels use this same formula
+__host__ __device__ inline int cand_nper(int64_t ncand, int64_t total) {
+  const int64_t n = total > 0 ? 256 * ncand / total : 0;
+  return n < 1 ? 1 : (int)n;
+}
 static_assert(SELECT_CLAIM_WORD < SELECT_ZERO_WORDS && SELECT_CLAIM_WORD != SELECT_CCOUNT_WORD, "cleared, unshared");
 // candidate mode: the score pass appended the candidate pairs (ScoreArgs::cand_off); one workgroup
 // per list, lists of at most SELECT_CAND_MAX_N candidates (an LDS bitmap over them)

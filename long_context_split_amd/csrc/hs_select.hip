@@ -373,7 +373,7 @@ __global__ __launch_bounds__(FIN_NT) void sel_cand_select_kernel(SelectArgs a) {
   __shared__ uint32_t s_maxc;
   const uint32_t* w = ws_list(a, list);
   const uint2* cand = (const uint2*)(w + a.cand_off);
-  const int nreg = a.cand_regions;                                // <= 256
+  const int nreg = (int)min(max(w[SELECT_NREG_WORD], 1u), 256u);  // the list's regions, from the score pass
   // the first-digit histogram is loaded first (it does not depend on the region counts) and searched
   // in LDS, so neither the counts nor the search wait for it
   uint32_t h1[2048 / FIN_NT];

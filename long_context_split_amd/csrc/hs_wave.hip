@@ -328,10 +328,22 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
   static_assert(!CAND || NQ == 1, "candidate mode: one query token");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int list, cidx, slot = 0, nper = 1;                            // lists own max(fold, ceil(ncand / chunk)) items
-  if constexpr (CAND) {
-    nper = (int)gridDim.x / a.n_lists;                           // workgroups per list, on consecutive XCDs
-    list = (int)blockIdx.x / nper;
-    slot = (int)blockIdx.x % nper;
+  if constexpr (CAND) {                                           // a list's workgroups: consecutive (and XCDs)
+    if (a.cand_uniform) {
+      nper = (int)gridDim.x / a.n_lists;
+      list = (int)blockIdx.x / nper;
+      slot = (int)blockIdx.x % nper;
+    } else {                                                     // prefix over the lists (n_lists <= 64)
+      int acc = 0;
+      list = a.n_lists - 1;
+      for (int l = 0; l < a.n_lists; ++l) {
+        const int L = a.seq_len[l / a.n_kv];
+        const int np = cand_nper(L - min(a.window, L), a.cand_total);
+        if ((int)blockIdx.x < acc + np) { list = l; nper = np; break; }
+        acc += np;
+      }
+      slot = (int)blockIdx.x - acc;
+    }
     cidx = slot;
   } else {
     grid_item(a.seq_len, a.n_kv, a.n_lists, a.chunk, a.window, a.part_ml ? 1 : 0, a.uniform_items, blockIdx.x, list,
@@ -441,6 +453,7 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
   if (CAND && wave == 0) {
     const int d = need_cand ? lower_digit(ghist, (uint32_t)kk, lane) : 2048;
     if (lane == 0) { s_kd = d; s_cc = 0u; s_claimed = 2u * NW; }
+    if (lane == 0 && slot == 0) ghist[SELECT_NREG_WORD] = (uint32_t)nper;
   }
   uint2* const region = CAND ? (uint2*)(ghist + a.cand_off) + (size_t)slot * a.cand_region : nullptr;
   for (int p = tid; p < 32 * 16; p += NT) {
@@ -673,8 +686,10 @@ int64_t scores_cand_region(int64_t s_stride, int nper) {
 
 hipError_t launch_scores_wave(const ScoreArgs& a, int kvt, hipStream_t st) {
   if (a.R > 32 || a.n_q > 4 || (kvt != KV_BF16 && kvt != KV_FP8)) return hipErrorInvalidValue;
-  if (a.cand_off > 0 && (a.n_q != 1 || !a.hist || a.chunk != scores_cand_chunk() || a.n_items % a.n_lists ||
-                         a.cand_region < scores_cand_region(a.s_stride, a.n_items / a.n_lists)))
+  if (a.cand_off > 0 &&
+      (a.n_q != 1 || !a.hist || a.chunk != scores_cand_chunk() || (a.cand_uniform && a.n_items % a.n_lists) ||
+       (a.cand_uniform && a.cand_region < scores_cand_region(a.s_stride, a.n_items / a.n_lists)) ||
+       (!a.cand_uniform && (a.n_lists > 64 || a.cand_total < 0))))
     return hipErrorInvalidValue;
   const int nq = a.n_q == 1 ? 1 : a.n_q == 2 ? 2 : 4;
   if (kvt == KV_BF16) {

@@ -142,30 +142,40 @@ def test_select_blocks_budgets_and_long_list():
     _check_blocks(x.reshape(1, 1, 1, -1), [L], 1, 1, 1024, 128)
 
 
-@pytest.mark.parametrize("n_q,H,L,B", [(1, 32, 40000, 16), (1, 32, 1153, 16), (1, 32, 300, 16), (2, 16, 40000, 16),
-                                       (1, 32, 9000, 272), (1, 32, 129, 16), (1, 32, 100, 16), (1, 32, 20000, 20),
-                                       (1, 32, 20000, 40)])
-def test_candidate_selection_paths_agree(n_q, H, L, B, monkeypatch):
+@pytest.mark.parametrize("n_q,H,L,B,ragged", [(1, 32, 40000, 16, False), (1, 32, 1153, 16, False),
+                                              (1, 32, 300, 16, False), (2, 16, 40000, 16, False),
+                                              (1, 32, 9000, 272, False), (1, 32, 129, 16, False),
+                                              (1, 32, 100, 16, False), (1, 32, 20000, 20, False),
+                                              (1, 32, 20000, 40, False), (1, 32, 40000, 5, False),
+                                              (1, 32, 60000, 8, True), (1, 32, 3000, 4, True),
+                                              (1, 32, 20000, 33, True)])
+def test_candidate_selection_paths_agree(n_q, H, L, B, ragged, monkeypatch):
     """The full layer's selection three ways: from the candidates the score pass appends (the
-    default for one query token, equal lengths and at least 16 lists; no dense scores stored),
-    the same with the dense scores requested, and the dense three-kernel radix select.  All give
-    identical lists, and the one with scores equals the oracle's selection on those scores.
+    default for one query token and at least 16 lists, lowered to 4 here so the few-list cases take
+    it too; no dense scores stored), the same with the dense scores requested, and the dense
+    three-kernel radix select.  All give identical lists,
+    and the one with scores equals the oracle's selection on those scores.
     L = 1153 leaves most score workgroups without work, L = 300 selects every candidate, 272 lists
     get one score workgroup each (almost every unit is taken from the list's counter), L = 129
     leaves one candidate and L = 100 none (the window takes every row), 20 and 40 lists get 12 and 6
-    score workgroups each (not aligned with the 8 XCDs); the last sequence has identical K rows, so
-    every score ties and the lowest indices must win."""
+    score workgroups each (not aligned with the 8 XCDs), 5 lists get 51 each; ragged batches (lengths
+    drawn in [L/8, L], a list's workgroup count proportional to its candidates; the 3000 case has
+    lists shorter than the budget); the last sequence has identical K rows, so every score ties
+    and the lowest indices must win."""
     import synth
     from long_context_split_amd import hysparse as hs
-    banner(f"candidate vs dense selection n_q={n_q} H={H} L={L} B={B}")
-    rng = np.random.default_rng(21 + n_q + L)
-    lens = [L] * B
-    k = rng.standard_normal((B * L, 1, 128)).astype(np.float32)
-    k[(B - 1) * L:] = k[(B - 1) * L]                              # identical rows: all scores tied
-    v = rng.standard_normal((B * L, 1, 128)).astype(np.float32)
+    banner(f"candidate vs dense selection n_q={n_q} H={H} L={L} B={B} ragged={ragged}")
+    monkeypatch.setenv("HS_CAND_MIN_LISTS", "4")
+    rng = np.random.default_rng(21 + n_q + L + B)
+    lens = [int(x) for x in rng.integers(max(1, L // 8), L + 1, B)] if ragged else [L] * B
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    tot = int(sum(lens))
+    k = rng.standard_normal((tot, 1, 128)).astype(np.float32)
+    k[starts[-1]:] = k[starts[-1]]                                # identical rows: all scores tied
+    v = rng.standard_normal((tot, 1, 128)).astype(np.float32)
     q = rng.standard_normal((B, n_q, H, 128)).astype(np.float32)
     dev = lambda x: torch.from_numpy(synth.bf16_bits(x).view(np.int16)).cuda().view(torch.bfloat16)
-    kv = hs.KVCache(dev(k), dev(v), lens)
+    kv = hs.KVCache(dev(k), dev(v), lens, starts)
     qd = dev(q)
     _, _, idx_a, cnt_a = hs.full_attn_select(kv, qd)
     S = hs.scores_stride(kv, 128)
@@ -178,10 +188,12 @@ def test_candidate_selection_paths_agree(n_q, H, L, B, monkeypatch):
     assert np.array_equal(ia, ib) and np.array_equal(ia, ic)
     assert np.array_equal(cnt_a.cpu().numpy(), cnt_c.cpu().numpy())
     scores = sc.cpu().numpy()
-    w, kk = selection.budget(L, 1024, 128)
     for i in range(B):
+        Li = lens[i]
+        w, kk = selection.budget(Li, 1024, 128)
         for t in range(n_q):
-            gi, gc = selection.select(np.ascontiguousarray(scores[i, t, 0, :L - w]), L, 1024, 128, f32_keys=True)
+            gi, gc = selection.select(np.ascontiguousarray(scores[i, t, 0, :Li - w]), Li, 1024, 128, f32_keys=True)
             assert np.array_equal(ia[i, t, 0], gi), f"seq {i} t {t}"
+    w, kk = selection.budget(lens[-1], 1024, 128)
     last = ia[-1, :, 0, :kk]
     assert np.array_equal(last, np.broadcast_to(np.arange(kk), last.shape))
