@@ -163,29 +163,6 @@ __device__ inline void grid_item(const int32_t* seq_len, int n_kv, int n_lists, 
 // Split-K partials of one attention row: chunk c holds (m_c, l_c) at ml[c * mstride] (running max in
 // log2 units, sum of 2^(s - m_c)) and acc_c = sum 2^(s - m_c) v at acc[c * astride].
 
-// log2 sum_c 2^m_c l_c over c < nch, by one wave (lanes over chunks, 4 loads per lane in flight);
-// the same value on every lane, -inf when nch == 0 or the sum is zero.
-__device__ inline float merged_lse2(const float* ml, size_t mstride, int nch, int lane) {
-  float mx = -INFINITY, ls = 0.f;
-  for (int c0 = 0; c0 < nch; c0 += 256) {
-    float2 v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = c0 + 64 * u + lane;
-      v[u] = *(const float2*)(ml + (size_t)min(c, nch - 1) * mstride);   // clamped: in bounds, no branch
-      if (c >= nch) v[u] = make_float2(-INFINITY, 0.f);
-    }
-    const float nm = fmaxf(mx, wave_max(fmaxf(fmaxf(v[0].x, v[1].x), fmaxf(v[2].x, v[3].x))));
-    if (nm == -INFINITY) continue;                                         // uniform over the wave
-    ls *= exp2f(mx - nm);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) ls += exp2f(v[u].x - nm) * v[u].y;
-    mx = nm;
-  }
-  ls = wave_sum(ls);
-  return ls > 0.f ? mx + __log2f(ls) : -INFINITY;
-}
-
 // One wave's share of a row's partials, chunks c = c_first, c_first + step, ... < nch, combined in a
 // single online pass (8 chunks in flight): running max m, l and o relative to it (lanes holding
 // d = 2 lane, 2 lane + 1).  m = -inf if the wave had no chunk.  m and l are the same on every lane.
