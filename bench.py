@@ -64,6 +64,8 @@ def parse():
                     help="evict the 256 MB Infinity Cache between steps by reading (default) or writing 1 GiB")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP-graph replay")
     ap.add_argument("--no-bridge", action="store_true", help="skip the KV Bridging measurement")
+    ap.add_argument("--select-block", type=int, default=0, choices=[0, 64],
+                    help="64: the block-level selection variant (whole 64-token blocks)")
     ap.add_argument("--bridge-iters", type=int, default=10)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device-to-device copy (known bytes, for scaling HBM counters)")
@@ -114,7 +116,7 @@ def main():
     # outputs and workspaces, allocated once
     for bl in blocks:
         kv = bl["kv"]
-        p = hs.params(H, n_q, top_k, window)
+        p = hs.params(H, n_q, top_k, window, select_block=args.select_block)
         bl["out"] = torch.empty((B, n_q, H, 128), dtype=torch.float32, device=dev)
         bl["lse"] = torch.empty((B, n_q, H), dtype=torch.float32, device=dev)
         bl["idx"] = torch.empty((B, n_q, 1, top_k + window), dtype=torch.int32, device=dev)
@@ -127,7 +129,7 @@ def main():
         for bl in blocks:
             kv = bl["kv"]
             hs.full_attn_select(kv, bl["qf"], top_k, window, out=bl["out"], lse=bl["lse"], sel_idx=bl["idx"],
-                                sel_count=bl["cnt"], ws=bl["ws_full"])
+                                sel_count=bl["cnt"], ws=bl["ws_full"], select_block=args.select_block)
             for i in range(n_sparse):
                 hs.sparse_attn(kv, bl["qs"][i], bl["idx"], bl["cnt"], top_k, window, out=bl["so"][i],
                                ws=bl["ws_sp"])
@@ -227,7 +229,7 @@ def main():
     roof = None
     if k1:
         sec = k1["avg_ms"] * 1e-3
-        default_workload = args.config == 2 and args.L is None and args.B is None
+        default_workload = args.config == 2 and args.L is None and args.B is None and not args.select_block
         traffic = KNOWN_TRAFFIC.get(kernel_digest()) if default_workload else None
         t_hbm, t_mfma = k1_bytes / (HBM_PEAK_GBPS * 1e9), k1_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
         if t_hbm >= t_mfma:
@@ -272,8 +274,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": spec["name"] if args.L is None and args.B is None else
-            f"{spec['name']}_L{args.L or 'cfg'}_B{args.B or 'cfg'}",
+            "workload": (spec["name"] if args.L is None and args.B is None else
+                         f"{spec['name']}_L{args.L or 'cfg'}_B{args.B or 'cfg'}") +
+                        (f"_block{args.select_block}" if args.select_block else ""),
             "batch": B, "seq_len": int(lens.max()) if args.config == 2 else [int(x) for x in lens],
             "query_heads": H, "kv_heads": 1, "head_dim": 128, "q_tokens": n_q, "top_k": top_k, "window": window,
             "sparse_layers": n_sparse, "blocks": n_blocks, "kv_dtype": spec["kv"],
