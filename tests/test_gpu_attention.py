@@ -266,6 +266,27 @@ def test_config3_full_size():
           f"recall {stats['hit'] / stats['tot']:.6f}", flush=True)
 
 
+@pytest.mark.slow
+def test_config5_full_size_sampled():
+    """Config 5 at full size in the benchmark's launch configuration: 8 ragged sequences of
+    64K-512K rows, bf16, H=32, 1 full + 5 sparse layers per block, each block with its own cache.
+    Blocks 0 and 3 run; the oracle checks each one's shortest and longest sequence."""
+    stats = {}
+    for blk in (0, 3):
+        banner(f"config 5 full size: block {blk}")
+        up = Uploaded(synth.decode_case(5, block=blk))
+        res = _run_block(up)
+        lens = up.case["lengths"]
+        for i in (int(np.argmin(lens)), int(np.argmax(lens))):
+            banner(f"config 5 block {blk}: oracle on sequence {i} (L={int(lens[i])})")
+            _check_seq(up, res, i, stats=stats)
+        del up, res
+        torch.cuda.empty_cache()
+    assert stats["hit"] / stats["tot"] >= 0.999
+    print(f"[result] config5 max|dO| {stats['err']:.3e} sparse {stats['serr']:.3e} "
+          f"recall {stats['hit'] / stats['tot']:.6f}", flush=True)
+
+
 def test_block_level_variant_bf16():
     """The earlier block-level selection through the full layer: lists equal the oracle's block
     selection on the GPU's own scores (float32 tree order), overlap the float64 block selection,
