@@ -9,17 +9,15 @@
 // stored at cache rows row_offset + t, as bf16 (round to nearest even) or as
 // OCP E4M3FN codes with one float32 scale per row (scale = amax / 448).
 //
-// Workgroup tile: 256 tokens x 256 columns (one target: K's 128 columns, then
-// V's), K-stage 64, 8 waves each owning 64 rows x 128 columns = one head block,
-// so a row's amax is reduced inside one wave; one workgroup per CU.  The stages
-// are double-buffered in LDS (one barrier per stage) and the global loads run
-// two stages ahead in two register buffers.  MFMA v_mfma_f32_32x32x16_bf16,
-// operands from LDS as 16-byte reads: A = rows of X, B = rows of W^T.  W is
-// stored transposed ([column][k]) at stage time: each thread loads the same
-// 8-column piece of two adjacent k rows and writes 32-bit (k, k+1) pairs; the
-// 16-byte k-quads of every 8-column group are XOR-swizzled by the group index,
-// which spreads both the transposing writes and the operand reads over the LDS
-// banks.
+// Workgroup tile: 256 tokens x 256 columns (one target: K's 128 columns, then V's), K-stage 64, 8 waves
+// each owning 64 rows x 128 columns = one head block, so a row's amax is reduced inside one wave; one
+// workgroup per CU.  The stages are double-buffered in LDS (one barrier per stage) and the global loads
+// run two stages ahead in two register buffers.  MFMA v_mfma_f32_32x32x16_bf16 with operands from LDS:
+// A = rows of X (16-byte reads, 144-byte row pitch); W is kept in its own [k][column] layout (576-byte
+// row pitch) and each B operand (8 consecutive k of one column) comes from two LDS transpose reads,
+// which on gfx950 hand each lane of a 16-lane group one column of a 4-row x 16-column block.
+// Tile order: the workgroups of one token tile (all targets) are adjacent in dispatch order and land
+// on one XCD, so they share that tile's X rows through the XCD's L2.
 
 #include "hs_common.hpp"
 #include "hs_internal.hpp"
@@ -29,18 +27,22 @@ namespace hs {
 namespace {
 constexpr int BM = 256, BN = 256, BK = 64, NT = 512;
 constexpr int AROW = BK * 2 + 16;               // 144 B per X row in LDS
-constexpr int BROW = BK * 2 + 16;               // 144 B per column of W^T in LDS
-constexpr int STAGE = BM * AROW + BN * BROW;    // 73728 B
+constexpr int WROW = 576;                       // bytes per k row of W (256 columns) in LDS
+constexpr int STAGE = BM * AROW + BK * WROW;
 constexpr int EPI = 8 * 64 * 128 * 2;           // per-wave 64 x 128 bf16 staging
 constexpr int SMEM = 2 * STAGE > EPI ? 2 * STAGE : EPI;
 constexpr int APT = BM * BK * 2 / 16 / NT;      // X pieces per thread per stage (4)
-constexpr int BPT = BK * BN * 2 / 16 / NT;      // W pieces per thread per stage (4: two k-row pairs)
+constexpr int BPT = BK * BN * 2 / 16 / NT;      // W pieces per thread per stage (4)
 static_assert(APT == 4 && BPT == 4, "load split");
 
 __device__ __forceinline__ int crow(int lane, int r) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
-// byte offset of k-quad qd (8 k values) of W^T column n: quads XOR-swizzled per 8-column group
-__device__ __forceinline__ int wt_off(int n, int qd) { return n * BROW + 16 * (qd ^ ((n >> 3) & 7)); }
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+__device__ __forceinline__ u32x2 read_tr(const char* p) {      // LDS transpose read of 4 k rows x 16 columns per 16 lanes
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p)));
+}
 
 struct Regs { u32x4 a[APT], b[BPT]; };
 }  // namespace
@@ -49,8 +51,18 @@ __global__ __launch_bounds__(NT) void bridge_kernel(BridgeArgs a) {
   __shared__ __align__(16) char smem[SMEM];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.x * BM;
-  const int tgt = blockIdx.y;
+  // tile order: groups of 8 token tiles x all targets are consecutive in dispatch order (x fastest), and
+  // dispatch id % 8 picks the XCD, so a tile's targets run together on one XCD
+  const int nt = a.n_targets, ntiles = gridDim.x;
+  int xt, tgt;
+  {
+    const int lin = blockIdx.y * ntiles + blockIdx.x;             // the hardware's dispatch order
+    const int grp = 8 * nt;                                       // ids per group: 8 tiles x nt targets
+    const int g = lin / grp, w = lin % grp;
+    if ((g + 1) * grp <= ntiles * nt) { xt = 8 * g + (w & 7); tgt = w >> 3; }
+    else { xt = lin / nt; tgt = lin % nt; }                       // the last partial group: plain order
+  }
+  const int64_t m0 = (int64_t)xt * BM;
   const uint16_t* wk = a.w[2 * tgt];
   const uint16_t* wv = a.w[2 * tgt + 1];
   const int Dm = a.Dm;
@@ -65,10 +77,9 @@ __global__ __launch_bounds__(NT) void bridge_kernel(BridgeArgs a) {
       r.a[i] = *(const u32x4*)(a.x + gr * Dm + k0 + c * 8);
     }
 #pragma unroll
-    for (int i = 0; i < BPT; ++i) {                               // pair i/2: k rows 2 kp, 2 kp + 1
-      const int q = tid + NT * (i >> 1), kp = q >> 5, np = q & 31;
-      const uint16_t* src = (np < 16 ? wk : wv) + (int64_t)(k0 + 2 * kp + (i & 1)) * D + (np & 15) * 8;
-      r.b[i] = *(const u32x4*)src;
+    for (int i = 0; i < BPT; ++i) {                               // k row p >> 5, 16-byte column chunk p & 31
+      const int p = tid + NT * i, kr = p >> 5, c = p & 31;
+      r.b[i] = *(const u32x4*)((c < 16 ? wk : wv) + (int64_t)(k0 + kr) * D + (c & 15) * 8);
     }
   };
   auto store = [&](const Regs& r, int buf) {
@@ -80,15 +91,9 @@ __global__ __launch_bounds__(NT) void bridge_kernel(BridgeArgs a) {
       *(u32x4*)(As + (p >> 3) * AROW + (p & 7) * 16) = r.a[i];
     }
 #pragma unroll
-    for (int jp = 0; jp < BPT / 2; ++jp) {                        // W^T: word (k, k + 1) of column n
-      const int q = tid + NT * jp, kp = q >> 5, np = q & 31;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t a0 = r.b[2 * jp][e >> 1], a1 = r.b[2 * jp + 1][e >> 1];
-        const uint32_t word = (e & 1) ? ((a0 >> 16) | (a1 & 0xFFFF0000u)) : ((a0 & 0xFFFFu) | (a1 << 16));
-        const int n = 8 * np + e;
-        *(uint32_t*)(Bs + wt_off(n, kp >> 2) + 4 * (kp & 3)) = word;
-      }
+    for (int i = 0; i < BPT; ++i) {
+      const int p = tid + NT * i;
+      *(u32x4*)(Bs + (p >> 5) * WROW + (p & 31) * 16) = r.b[i];
     }
   };
   f32x16 acc[2][4] = {};
@@ -102,9 +107,12 @@ __global__ __launch_bounds__(NT) void bridge_kernel(BridgeArgs a) {
       for (int i = 0; i < 2; ++i)
         av[i] = *(const s16x8*)(As + (64 * wm + 32 * i + (lane & 31)) * AROW + (16 * s + 8 * (lane >> 5)) * 2);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = 128 * wn + 32 * j + (lane & 31);
-        bv[j] = *(const s16x8*)(Bs + wt_off(n, 2 * s + (lane >> 5)));
+      for (int j = 0; j < 4; ++j) {                               // k = 16 s + 8 (lane >> 5) + 0..7, column 128 wn + 32 j + (lane & 31)
+        const char* p = Bs + (16 * s + 8 * (lane >> 5) + ((lane & 15) >> 2)) * WROW +
+                        (128 * wn + 32 * j + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+        const u32x2 lo = read_tr(p), hi = read_tr(p + 4 * WROW);
+        const u32x4 q = {lo[0], lo[1], hi[0], hi[1]};
+        bv[j] = __builtin_bit_cast(s16x8, q);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)

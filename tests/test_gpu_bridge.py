@@ -124,6 +124,23 @@ def test_random_xavier_weights(fp8):
     print(f"[result] bridge fp8={fp8} equal fraction {frac:.5f}", flush=True)
 
 
+@pytest.mark.parametrize("T,nt", [(2600, 3), (4700, 5)])
+def test_tile_order_with_partial_group(T, nt):
+    """Workgroups run in groups of 8 token tiles x all targets; 11 and 19 tiles leave a partial last
+    group (plain order) after full ones.  Every row of every target is checked against the oracle."""
+    banner(f"bridge tile order T={T} D=256 targets={nt}")
+    from long_context_split_amd import hysparse as hs
+    case = synth.bridge_case(4, T=T, D=256, n_targets=nt)
+    off, cap = 7, T + 50
+    tg = _targets(nt, cap, True)
+    hs.kv_bridge(dev_bf16(case["x"]), [dev_bf16(w) for w in case["w_k"]], [dev_bf16(w) for w in case["w_v"]],
+                 tg, off)
+    torch.cuda.synchronize()
+    frac = _check_random(case, tg, off, True)
+    assert frac >= 0.99
+    print(f"[result] bridge T={T} targets={nt} equal fraction {frac:.5f}", flush=True)
+
+
 @pytest.mark.slow
 def test_config4_full_size_sampled_rows():
     """Config 4: 32768 tokens x 4096 -> 4 targets x (K, V), FP8, into 1M-row caches at
