@@ -141,6 +141,23 @@ def test_tile_order_with_partial_group(T, nt):
     print(f"[result] bridge T={T} targets={nt} equal fraction {frac:.5f}", flush=True)
 
 
+@pytest.mark.parametrize("D,fp8", [(64, True), (192, True), (192, False), (320, True)])
+def test_odd_stage_counts(D, fp8):
+    """d_model 64, 192, 320: 1, 3 and 5 K-stages of 64, so the stage loop leaves through its odd exit
+    (the two-stage register lead re-reads the last stage past the end)."""
+    banner(f"bridge stages D={D} T=700 targets=2 fp8={fp8}")
+    from long_context_split_amd import hysparse as hs
+    case = synth.bridge_case(4, T=700, D=D, n_targets=2)
+    off, cap = 3, 760
+    tg = _targets(2, cap, fp8)
+    hs.kv_bridge(dev_bf16(case["x"]), [dev_bf16(w) for w in case["w_k"]], [dev_bf16(w) for w in case["w_v"]],
+                 tg, off)
+    torch.cuda.synchronize()
+    frac = _check_random(case, tg, off, fp8)
+    assert frac >= 0.99
+    print(f"[result] bridge D={D} fp8={fp8} equal fraction {frac:.5f}", flush=True)
+
+
 @pytest.mark.slow
 def test_config4_full_size_sampled_rows():
     """Config 4: 32768 tokens x 4096 -> 4 targets x (K, V), FP8, into 1M-row caches at
