@@ -223,6 +223,25 @@ hs_status hs_sparse_attn(const hs_kv_cache *kv, const hs_attn_params *p, const v
                          hs_dtype q_dtype, const int32_t *sel_idx, const int32_t *sel_count,
                          float *out, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Sliding-window attention of the Self-Decoder side, which feeds KV Bridging
+ * (ithome page, architecture overview: the Self-Decoder mixes full and
+ * sliding-window attention over the current input; the pages give no window
+ * size, so w = p->window is the caller's).  The q_tokens queries of sequence b
+ * are the last q_tokens rows of its cache (a prefill chunk appended before the
+ * call): query t sits at position pos = L_b - q_tokens + t and, for every head h
+ * of KV head g,
+ *     out[b,t,h] = sum_{j in B} softmax_B(l)_j v[b,j,g],  l_j = scale * <q, k_j>,
+ *     B = { max(0, pos - w + 1) .. pos }.
+ *   q   device [B, q_tokens, num_q_heads, head_dim], q_dtype HS_BF16
+ *   out device float [B, q_tokens, num_q_heads, head_dim]
+ * p->top_k and p->select_block are ignored.  No workspace.  Cache dtypes:
+ * HS_BF16, HS_FP8_E4M3.  Errors: HS_ERR_INVALID_ARGUMENT (null pointer, bad
+ * shape, window < 1, q_tokens > L_b for some b, L_b < 1, rows outside
+ * capacity, scale pointers not matching the dtype), HS_ERR_UNSUPPORTED
+ * (head_dim != 128, an F32 cache, F32 queries). */
+hs_status hs_swa_attn(const hs_kv_cache *kv, const hs_attn_params *p, const void *q,
+                      hs_dtype q_dtype, float *out, void *stream);
+
 /* The selection stage alone, on caller-given float32 scores (a test hook for
  * checking the selection bit for bit).  scores: device float
  * [batch, q_tokens, n_kv, max_len - min(window, max_len)] laid out as

@@ -621,6 +621,42 @@ hs_status hs_sparse_attn(const hs_kv_cache* kv, const hs_attn_params* p, const v
   return HS_OK;
 }
 
+hs_status hs_swa_attn(const hs_kv_cache* kv, const hs_attn_params* p, const void* q, hs_dtype q_dtype,
+                      float* out, void* stream) {
+  g_last_error.clear();
+  CacheInfo ci;
+  hs_status st = check_cache(kv, ci, true);
+  if (st != HS_OK) return st;
+  if (!p) return fail(HS_ERR_INVALID_ARGUMENT, "params is NULL");
+  if (p->num_q_heads < 1 || p->num_q_heads % ci.n_kv)
+    return fail(HS_ERR_INVALID_ARGUMENT, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
+                p->num_q_heads, ci.n_kv);
+  if (p->window < 1) return fail(HS_ERR_INVALID_ARGUMENT, "window %d must be >= 1", p->window);
+  if (!(p->softmax_scale >= 0.f) || !isfinite(p->softmax_scale))
+    return fail(HS_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
+  if (p->q_tokens < 1) return fail(HS_ERR_INVALID_ARGUMENT, "q_tokens %d", p->q_tokens);
+  for (int b = 0; b < kv->batch; ++b)
+    if (p->q_tokens > kv->h_seq_len[b])
+      return fail(HS_ERR_INVALID_ARGUMENT, "q_tokens %d > seq_len[%d] = %d", p->q_tokens, b, kv->h_seq_len[b]);
+  if (!q || !out) return fail(HS_ERR_INVALID_ARGUMENT, "q/out is NULL");
+  if (q_dtype != HS_BF16) return fail(HS_ERR_UNSUPPORTED, "q dtype must be BF16");
+  if (kv->dtype == HS_F32) return fail(HS_ERR_UNSUPPORTED, "F32 caches are not supported here");
+  if (!aligned16(q) || !aligned16(out)) return fail(HS_ERR_INVALID_ARGUMENT, "q/out not 16-byte aligned");
+  if ((int64_t)kv->batch * ci.n_kv > 65535) return fail(HS_ERR_UNSUPPORTED, "batch * num_kv_heads > 65535");
+  hs::AttnArgs a{};
+  a.k = kv->k; a.v = kv->v; a.k_scale = kv->k_scale; a.v_scale = kv->v_scale;
+  a.row_start = kv->d_row_start; a.seq_len = kv->d_seq_len;
+  a.q = q; a.q_f32 = 0;
+  a.n_kv = ci.n_kv; a.H = p->num_q_heads; a.G = p->num_q_heads / ci.n_kv; a.n_q = p->q_tokens;
+  a.R = a.G; a.n_lists = kv->batch * ci.n_kv;
+  a.scale_log2 = scale_log2(p);
+  a.out = out; a.window = p->window;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = timed("swa_attn", s, [&] { return hs::launch_swa_attn(a, kv_type(kv->dtype), s); });
+  if (e != hipSuccess) return hip_fail(e, "sliding-window attention");
+  return HS_OK;
+}
+
 hs_status hs_select_from_scores(const float* scores, const int32_t* d_seq_len, const int32_t* h_seq_len,
                                 int32_t batch, int32_t q_tokens, int32_t n_kv, int32_t max_len, int32_t top_k,
                                 int32_t window, int32_t select_block, int32_t* sel_idx, int32_t* sel_count,

@@ -39,6 +39,7 @@ struct AttnArgs {
   uint32_t* zero_ptr;    // attn_wave: words cleared by the grid (nullable):
   int64_t zero_stride;   //   zero_lists runs of zero_words words, zero_stride apart
   int zero_words, zero_lists;
+  int window;            // swa_attn: band width w (rows p - w + 1 .. p)
 };
 
 struct MergeArgs {
@@ -155,6 +156,7 @@ hipError_t launch_attn_partial(const AttnArgs& a, int kvt, int ct, int nwr, bool
 hipError_t launch_attn_wave(const AttnArgs& a, int kvt, hipStream_t st);
 // sparse layer, bf16 Q with a bf16 or FP8 cache, any G (blocks of 32 heads); chunk a multiple of 32
 hipError_t launch_attn_gather(const AttnArgs& a, int kvt, hipStream_t st);
+hipError_t launch_swa_attn(const AttnArgs& a, int kvt, hipStream_t st);
 hipError_t launch_attn_merge(const MergeArgs& m, hipStream_t st);
 // attn_rows: dense pass 1 for R > 32 query rows per list, bf16 or FP8 caches, bf16 MFMA;
 // nrg = query-row groups of 32 per workgroup (2, 4 or 8; rows beyond 32*nrg take more z blocks)

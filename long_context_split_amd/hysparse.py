@@ -82,6 +82,8 @@ lib.hs_full_attn_select.restype = ctypes.c_int
 lib.hs_full_attn_select.argtypes = [_KVP, _PP, _P, ctypes.c_int, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
 lib.hs_sparse_attn.restype = ctypes.c_int
 lib.hs_sparse_attn.argtypes = [_KVP, _PP, _P, ctypes.c_int, _P, _P, _P, _P, ctypes.c_size_t, _P]
+lib.hs_swa_attn.restype = ctypes.c_int
+lib.hs_swa_attn.argtypes = [_KVP, _PP, _P, ctypes.c_int, _P, _P]
 lib.hs_select_from_scores.restype = ctypes.c_int
 lib.hs_select_from_scores.argtypes = [_P, _P, ctypes.POINTER(ctypes.c_int32)] + [ctypes.c_int32] * 7 + \
     [_P, _P, _P, ctypes.c_size_t, _P]
@@ -256,6 +258,17 @@ def sparse_attn(kv, q, sel_idx, sel_count, top_k=1024, window=128, softmax_scale
         ws = workspace(sparse_attn_workspace_size(kv, p), dev)
     check(lib.hs_sparse_attn(kv.c, ctypes.byref(p), _ptr(q), query_dtype(q), _ptr(sel_idx), _ptr(sel_count),
                              _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def swa_attn(kv, q, window, softmax_scale=0.0, out=None, stream=None):
+    """Sliding-window attention of the last q_tokens cache rows of every sequence (band of `window`
+    rows ending at each query's own row).  Returns out [B, n_q, H, 128] float32."""
+    B, n_q, H, d = q.shape
+    p = params(H, n_q, 0, window, softmax_scale)
+    if out is None:
+        out = torch.empty((B, n_q, H, d), dtype=torch.float32, device=q.device)
+    check(lib.hs_swa_attn(kv.c, ctypes.byref(p), _ptr(q), query_dtype(q), _ptr(out), _stream(stream)))
     return out
 
 
