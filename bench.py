@@ -29,7 +29,7 @@ METRIC = "hybrid-block decode queries/s + achieved HBM GB/s at 128K–1M ctx, 1 
 # HBM bytes per launch of the dense split-K pass at the default workload, from two
 # rocprofv3 --pmc runs (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors read off a
 # plain 1 GiB copy), keyed by a digest of the kernel sources they were taken on.
-KNOWN_TRAFFIC = {"cda23b8b0ccf622b": 2154592270}
+KNOWN_TRAFFIC = {"cb08ac1364f44c2f": 2154594332}
 KERNEL_SOURCES = ["long_context_split_amd/csrc/hs_wave.hip", "long_context_split_amd/csrc/hs_mfma.hpp",
                   "long_context_split_amd/csrc/hs_common.hpp", "long_context_split_amd/csrc/hs_internal.hpp"]
 
@@ -64,6 +64,7 @@ def parse():
                     help="evict the 256 MB Infinity Cache between steps by reading (default) or writing 1 GiB")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP-graph replay")
     ap.add_argument("--no-bridge", action="store_true", help="skip the KV Bridging measurement")
+    ap.add_argument("--no-swa", action="store_true", help="skip the sliding-window attention measurement")
     ap.add_argument("--select-block", type=int, default=0, choices=[0, 64],
                     help="64: the block-level selection variant (whole 64-token blocks)")
     ap.add_argument("--bridge-iters", type=int, default=10)
@@ -247,6 +248,7 @@ def main():
 
     # ---------------------------------------------------------------- KV Bridging (prefill side)
     bridge = None if args.no_bridge else bench_bridge(dev, args.bridge_iters)
+    swa = None if args.no_swa else bench_swa(dev, args.bridge_iters)
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -290,6 +292,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "bridge": bridge,
+        "swa": swa,
         "timing": ("HIP-graph replay of the step" if graph is not None else "eager launches") +
                   "; HIP events per step" + ("" if args.flush == "none" else
                                              f"; Infinity Cache flushed between steps by a 1 GiB {args.flush}") +
@@ -387,6 +390,40 @@ def bench_bridge(dev, iters):
             "decode_append": {"workload": f"{nb} new tokens x 4096 -> 4 targets (K,V), FP8, scattered rows",
                               "us": round(ms_app * 1e3, 2), "bytes": app_bytes,
                               "GBps": round(app_bytes / (ms_app * 1e-3) / 1e9, 1), "bound": "hbm (weights)"}}
+
+
+def bench_swa(dev, iters):
+    """Self-Decoder sliding-window attention of a 32768-token prefill chunk over its own 32768-row bf16
+    cache: H = 32 query heads on one KV head, window 128 (seeded normal Q, K, V)."""
+    import torch
+    from long_context_split_amd import hysparse as hs
+    T, H, w = 32768, 32, 128
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    k = torch.randn((T, 1, 128), generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn((T, 1, 128), generator=g, device=dev).to(torch.bfloat16)
+    q = torch.randn((1, T, H, 128), generator=g, device=dev).to(torch.bfloat16)
+    kv = hs.KVCache(k, v, [T], [0])
+    out = torch.empty((1, T, H, 128), dtype=torch.float32, device=dev)
+    for _ in range(2):
+        hs.swa_attn(kv, q, w, out=out)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in evs:
+        a.record()
+        hs.swa_attn(kv, q, w, out=out)
+        b.record()
+    torch.cuda.synchronize()
+    ms = statistics.median(a.elapsed_time(b) for a, b in evs)
+    nbytes = T * H * 128 * 2 + T * H * 128 * 4 + 2 * T * 128 * 2      # Q in, O out, K and V once
+    band = sum(min(t + 1, w) for t in range(T))
+    flops = 4.0 * band * H * 128                                       # Q K^T and P V over each band
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    log(f"swa: {ms * 1e3:.1f} us  {gbps:.0f} GB/s  ({gbps / HBM_PEAK_GBPS:.3f} of HBM peak)")
+    return {"workload": "swa_chunk_32k: 32768-token chunk over its 32768-row bf16 cache, H=32, n_kv=1, window 128",
+            "us": round(ms * 1e3, 2), "bound": "hbm", "GBps": round(gbps, 1), "peak_GBps": HBM_PEAK_GBPS,
+            "frac": round(gbps / HBM_PEAK_GBPS, 4), "bytes": nbytes, "flops": flops,
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
 
 
 def cpu_baseline(case, spec, top_k, window, budget_s):
