@@ -238,7 +238,8 @@ hs_status hs_sparse_attn(const hs_kv_cache *kv, const hs_attn_params *p, const v
  * HS_BF16, HS_FP8_E4M3.  Errors: HS_ERR_INVALID_ARGUMENT (null pointer, bad
  * shape, window < 1, q_tokens > L_b for some b, L_b < 1, rows outside
  * capacity, scale pointers not matching the dtype), HS_ERR_UNSUPPORTED
- * (head_dim != 128, an F32 cache, F32 queries). */
+ * (head_dim != 128, an F32 cache, F32 queries, batch * num_kv_heads > 65535).
+ * Launch failures: HS_ERR_HIP. */
 hs_status hs_swa_attn(const hs_kv_cache *kv, const hs_attn_params *p, const void *q,
                       hs_dtype q_dtype, float *out, void *stream);
 
