@@ -65,6 +65,7 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP-graph replay")
     ap.add_argument("--no-bridge", action="store_true", help="skip the KV Bridging measurement")
     ap.add_argument("--no-swa", action="store_true", help="skip the sliding-window attention measurement")
+    ap.add_argument("--swa-window", type=int, default=128, help="window of the sliding-window measurement")
     ap.add_argument("--select-block", type=int, default=0, choices=[0, 64],
                     help="64: the block-level selection variant (whole 64-token blocks)")
     ap.add_argument("--bridge-iters", type=int, default=10)
@@ -248,7 +249,7 @@ def main():
 
     # ---------------------------------------------------------------- KV Bridging (prefill side)
     bridge = None if args.no_bridge else bench_bridge(dev, args.bridge_iters)
-    swa = None if args.no_swa else bench_swa(dev, args.bridge_iters)
+    swa = None if args.no_swa else bench_swa(dev, args.bridge_iters, args.swa_window)
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -392,12 +393,12 @@ def bench_bridge(dev, iters):
                               "GBps": round(app_bytes / (ms_app * 1e-3) / 1e9, 1), "bound": "hbm (weights)"}}
 
 
-def bench_swa(dev, iters):
+def bench_swa(dev, iters, w=128):
     """Self-Decoder sliding-window attention of a 32768-token prefill chunk over its own 32768-row bf16
     cache: H = 32 query heads on one KV head, window 128 (seeded normal Q, K, V)."""
     import torch
     from long_context_split_amd import hysparse as hs
-    T, H, w = 32768, 32, 128
+    T, H = 32768, 32
     g = torch.Generator(device=dev)
     g.manual_seed(1234)
     k = torch.randn((T, 1, 128), generator=g, device=dev).to(torch.bfloat16)
@@ -420,7 +421,7 @@ def bench_swa(dev, iters):
     flops = 4.0 * band * H * 128                                       # Q K^T and P V over each band
     gbps = nbytes / (ms * 1e-3) / 1e9
     log(f"swa: {ms * 1e3:.1f} us  {gbps:.0f} GB/s  ({gbps / HBM_PEAK_GBPS:.3f} of HBM peak)")
-    return {"workload": "swa_chunk_32k: 32768-token chunk over its 32768-row bf16 cache, H=32, n_kv=1, window 128",
+    return {"workload": f"swa_chunk_32k: 32768-token chunk over its 32768-row bf16 cache, H=32, n_kv=1, window {w}",
             "us": round(ms * 1e3, 2), "bound": "hbm", "GBps": round(gbps, 1), "peak_GBps": HBM_PEAK_GBPS,
             "frac": round(gbps / HBM_PEAK_GBPS, 4), "bytes": nbytes, "flops": flops,
             "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
