@@ -119,8 +119,10 @@ typedef struct {
   int32_t select_block;
 } hs_attn_params;
 
-/* Workspace bytes hs_full_attn_select needs for these shapes (0 on invalid
- * arguments).  Uses the host lengths only. */
+/* Workspace bytes hs_full_attn_select needs for these shapes: the largest over
+ * the query types that are supported for them (0 when none is, or on invalid
+ * arguments).  Uses the host lengths only.  The size queries do not change the
+ * calling thread's last error. */
 size_t hs_full_attn_select_workspace_size(const hs_kv_cache *kv, const hs_attn_params *p);
 
 /* Workspace bytes hs_sparse_attn needs for these shapes (0 on invalid arguments). */
@@ -201,10 +203,13 @@ hs_status hs_kv_append(const void *hidden, int64_t n_tokens, int32_t d_model, in
  *             S = max_b (L_b - min(window, L_b)); when given, the float32 s_j
  *             used for selection are left there (entries past a list's own
  *             candidate count are unspecified)
- * Cache dtypes: HS_F32, HS_BF16, HS_FP8_E4M3.  Errors: HS_ERR_INVALID_ARGUMENT
- * (null pointer, bad shape, L_b < 1, rows outside capacity, scale pointers not
- * matching the dtype, top_k/window < 0), HS_ERR_WORKSPACE_TOO_SMALL,
- * HS_ERR_UNSUPPORTED (head_dim != 128). */
+ * Cache dtypes: HS_F32, HS_BF16, HS_FP8_E4M3.  Heads per KV head G = H / n_kv:
+ * 8, 16, 32, 64, 128 or 256 (at most 128 with F32 queries or an F32 cache).
+ * Alignment: q and out 16 bytes; lse, sel_idx, sel_count and scores_out 4 bytes.
+ * Errors: HS_ERR_INVALID_ARGUMENT (null pointer, misaligned pointer, bad shape,
+ * L_b < 1, rows outside capacity, scale pointers not matching the dtype,
+ * top_k/window < 0), HS_ERR_WORKSPACE_TOO_SMALL, HS_ERR_UNSUPPORTED (head_dim !=
+ * 128, another G, more than 65535 lists B * q_tokens * num_kv_heads). */
 hs_status hs_full_attn_select(const hs_kv_cache *kv, const hs_attn_params *p, const void *q,
                               hs_dtype q_dtype, float *out, float *lse, int32_t *sel_idx,
                               int32_t *sel_count, float *scores_out, void *workspace,
@@ -218,7 +223,9 @@ hs_status hs_full_attn_select(const hs_kv_cache *kv, const hs_attn_params *p, co
  *     out[b,t,h] = sum_{j in S} softmax_S(l)_j v[b,j,g],  l_j = scale * <q, k_j>.
  *   q, out, sel_idx, sel_count: layouts as in hs_full_attn_select; every
  *   listed index must be in [0, L_b) (checked on the device: an index out of
- *   range is treated as absent).  Errors as hs_full_attn_select. */
+ *   range is treated as absent).  A list with no row left (count <= 0, or every
+ *   listed index absent) gets out = 0.  Any G.  Alignment: q and out 16 bytes,
+ *   sel_idx and sel_count 4 bytes.  Errors as hs_full_attn_select. */
 hs_status hs_sparse_attn(const hs_kv_cache *kv, const hs_attn_params *p, const void *q,
                          hs_dtype q_dtype, const int32_t *sel_idx, const int32_t *sel_count,
                          float *out, void *workspace, size_t workspace_bytes, void *stream);
@@ -249,7 +256,9 @@ hs_status hs_swa_attn(const hs_kv_cache *kv, const hs_attn_params *p, const void
  * scores_out above; lists with L_b = d_seq_len[b] use their first
  * L_b - min(window, L_b) entries.  Scores must be finite; the order is the
  * float order (-0 below +0), ties to the lower index.  select_block as in
- * hs_attn_params (0: tokens, 64: blocks).  Outputs as hs_full_attn_select. */
+ * hs_attn_params (0: tokens, 64: blocks).  Outputs as hs_full_attn_select.
+ * scores, sel_idx and sel_count must be 4-byte aligned; at most 65535 lists
+ * (HS_ERR_UNSUPPORTED beyond). */
 hs_status hs_select_from_scores(const float *scores, const int32_t *d_seq_len,
                                 const int32_t *h_seq_len, int32_t batch, int32_t q_tokens,
                                 int32_t n_kv, int32_t max_len, int32_t top_k, int32_t window,
@@ -261,7 +270,8 @@ hs_status hs_select_from_scores(const float *scores, const int32_t *d_seq_len,
  * the same stream.  hs_timing_collect waits for the recorded events, writes up
  * to max records (kernel name, milliseconds) in launch order, returns how many
  * it wrote (-1 on a HIP error) and forgets all records.  The name pointers are
- * static strings.  Not for concurrent use from several threads. */
+ * static strings.  The switch and the records belong to the calling thread (like
+ * the last error): a thread collects only the launches it made itself. */
 typedef struct {
   const char *name;
   float ms;

@@ -10,7 +10,6 @@
 #include <string.h>
 
 #include <algorithm>
-#include <mutex>
 #include <string>
 #include <vector>
 
@@ -38,14 +37,15 @@ hs_status hip_fail(hipError_t e, const char* what) {
 
 // ---------------------------------------------------------------- optional kernel timing
 
-std::mutex g_tmu;
-bool g_timing = false;
+// Per calling thread, like the last error: each thread enables, records and collects its own
+// launches (its events are kept in its own pool for reuse).
+thread_local bool g_timing = false;
 struct TimeRec {
   const char* name;
   hipEvent_t a, b;
 };
-std::vector<TimeRec> g_recs;
-std::vector<hipEvent_t> g_pool;
+thread_local std::vector<TimeRec> g_recs;
+thread_local std::vector<hipEvent_t> g_pool;
 
 hipEvent_t pool_get() {
   if (!g_pool.empty()) {
@@ -62,7 +62,6 @@ hipEvent_t pool_get() {
 template <class F>
 hipError_t timed(const char* name, hipStream_t s, F&& launch) {
   if (!g_timing) return launch();
-  std::lock_guard<std::mutex> lk(g_tmu);
   hipEvent_t a = pool_get(), b = pool_get();
   if (!a || !b) return hipErrorOutOfMemory;
   hipError_t e = hipEventRecord(a, s);
@@ -76,6 +75,10 @@ hipError_t timed(const char* name, hipStream_t s, F&& launch) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+// Kernels put lists on the second grid dimension (at most 65535 blocks).
+constexpr int64_t MAX_LISTS = 65535;
 
 int env_int(const char* name, int dflt) {
   const char* s = getenv(name);
@@ -177,9 +180,11 @@ hs_status plan_full(const hs_kv_cache* kv, const hs_attn_params* p, hs_dtype q_d
   pl.G = H / ci.n_kv;
   pl.R = p->q_tokens * pl.G;
   pl.ct = (kv->dtype == HS_F32 || q_dtype == HS_F32) ? hs::CT_F32 : hs::CT_BF16;
-  if (!(pl.G % 32 == 0 || pl.G == 8 || pl.G == 16) || pl.G > 256)
-    return fail(HS_ERR_UNSUPPORTED, "heads per KV head G = %d: selection scores need G in {8, 16} or a "
-                "multiple of 32 up to 256", pl.G);
+  // The many-row score kernel sums a query token's heads inside one workgroup of 32 * 2^i rows, so
+  // a token's G rows must not straddle two workgroups: G is a power of two.
+  if (!(pl.G == 8 || pl.G == 16 || pl.G == 32 || pl.G == 64 || pl.G == 128 || pl.G == 256))
+    return fail(HS_ERR_UNSUPPORTED, "heads per KV head G = %d: selection scores need G in {8, 16, 32, 64, "
+                "128, 256}", pl.G);
   if (pl.ct == hs::CT_F32 && pl.G > 128)
     return fail(HS_ERR_UNSUPPORTED, "fp32 queries/caches support at most 128 heads per KV head");
   pl.nwr = pl.ct == hs::CT_F32 ? (pl.R <= 32 ? 1 : 4) : hs::rows_per_wave_group(pl.R);
@@ -380,13 +385,9 @@ const char* hs_status_string(hs_status s) {
 
 const char* hs_last_error(void) { return g_last_error.c_str(); }
 
-void hs_timing_enable(int enable) {
-  std::lock_guard<std::mutex> lk(g_tmu);
-  g_timing = enable != 0;
-}
+void hs_timing_enable(int enable) { g_timing = enable != 0; }
 
 int hs_timing_collect(hs_kernel_time* out, int max) {
-  std::lock_guard<std::mutex> lk(g_tmu);
   int n = 0;
   bool ok = true;
   for (const TimeRec& r : g_recs) {
@@ -401,23 +402,35 @@ int hs_timing_collect(hs_kernel_time* out, int max) {
 }
 
 size_t hs_full_attn_select_workspace_size(const hs_kv_cache* kv, const hs_attn_params* p) {
+  // a size query leaves the caller's last error as it was
+  const std::string saved = g_last_error;
+  size_t need = 0;
   CacheInfo ci;
-  if (check_cache(kv, ci, true) != HS_OK || check_params(p, ci.n_kv) != HS_OK) return 0;
-  FullPlan pl;
-  // the plan depends on the query type only through the compute type; size for the larger
-  if (plan_full(kv, p, HS_F32, ci, pl) != HS_OK) return 0;
-  FullPlan pb;
-  if (plan_full(kv, p, HS_BF16, ci, pb) != HS_OK) return 0;
-  return std::max(pl.total, pb.total);
+  if (check_cache(kv, ci, true) == HS_OK && check_params(p, ci.n_kv) == HS_OK) {
+    // The plan depends on the query type only through the compute type: each plan is sized on its
+    // own (fp32 plans reject more than 128 heads per KV head, bf16 plans allow 256), and the
+    // largest plan that exists is the answer.
+    for (hs_dtype qt : {HS_F32, HS_BF16}) {
+      FullPlan pl;
+      if (plan_full(kv, p, qt, ci, pl) == HS_OK) need = std::max(need, pl.total);
+    }
+  }
+  g_last_error = saved;
+  return need;
 }
 
 size_t hs_sparse_attn_workspace_size(const hs_kv_cache* kv, const hs_attn_params* p) {
+  const std::string saved = g_last_error;
+  size_t need = 0;
   CacheInfo ci;
-  if (check_cache(kv, ci, true) != HS_OK || check_params(p, ci.n_kv) != HS_OK) return 0;
-  SparsePlan a, b;
-  plan_sparse(kv, p, HS_F32, ci, a);
-  plan_sparse(kv, p, HS_BF16, ci, b);
-  return std::max(a.total, b.total);
+  if (check_cache(kv, ci, true) == HS_OK && check_params(p, ci.n_kv) == HS_OK) {
+    SparsePlan a, b;
+    plan_sparse(kv, p, HS_F32, ci, a);
+    plan_sparse(kv, p, HS_BF16, ci, b);
+    need = std::max(a.total, b.total);
+  }
+  g_last_error = saved;
+  return need;
 }
 
 size_t hs_select_workspace_size(int32_t batch, int32_t q_tokens, int32_t n_kv, int32_t max_len, int32_t top_k,
@@ -439,6 +452,12 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
   if (!q || !out || !sel_idx || !sel_count) return fail(HS_ERR_INVALID_ARGUMENT, "q/out/sel_idx/sel_count is NULL");
   if (q_dtype != HS_F32 && q_dtype != HS_BF16) return fail(HS_ERR_INVALID_ARGUMENT, "q dtype must be F32 or BF16");
   if (!aligned16(q)) return fail(HS_ERR_INVALID_ARGUMENT, "q not 16-byte aligned");
+  if (!aligned16(out)) return fail(HS_ERR_INVALID_ARGUMENT, "out not 16-byte aligned");
+  if (!aligned4(lse) || !aligned4(sel_idx) || !aligned4(sel_count) || !aligned4(scores_out))
+    return fail(HS_ERR_INVALID_ARGUMENT, "lse/sel_idx/sel_count/scores_out not 4-byte aligned");
+  if ((int64_t)ci.B * p->q_tokens * ci.n_kv > MAX_LISTS)
+    return fail(HS_ERR_UNSUPPORTED, "batch * q_tokens * num_kv_heads = %lld selection lists (at most %lld)",
+                (long long)ci.B * p->q_tokens * ci.n_kv, (long long)MAX_LISTS);
   FullPlan pl;
   if ((st = plan_full(kv, p, q_dtype, ci, pl)) != HS_OK) return st;
   if ((st = check_block_select(p->select_block, pl.s_stride)) != HS_OK) return st;
@@ -580,6 +599,12 @@ hs_status hs_sparse_attn(const hs_kv_cache* kv, const hs_attn_params* p, const v
   if (!q || !out || !sel_idx || !sel_count) return fail(HS_ERR_INVALID_ARGUMENT, "q/out/sel_idx/sel_count is NULL");
   if (q_dtype != HS_F32 && q_dtype != HS_BF16) return fail(HS_ERR_INVALID_ARGUMENT, "q dtype must be F32 or BF16");
   if (!aligned16(q)) return fail(HS_ERR_INVALID_ARGUMENT, "q not 16-byte aligned");
+  if (!aligned16(out)) return fail(HS_ERR_INVALID_ARGUMENT, "out not 16-byte aligned");
+  if (!aligned4(sel_idx) || !aligned4(sel_count))
+    return fail(HS_ERR_INVALID_ARGUMENT, "sel_idx/sel_count not 4-byte aligned");
+  if ((int64_t)ci.B * p->q_tokens * ci.n_kv > MAX_LISTS)
+    return fail(HS_ERR_UNSUPPORTED, "batch * q_tokens * num_kv_heads = %lld selection lists (at most %lld)",
+                (long long)ci.B * p->q_tokens * ci.n_kv, (long long)MAX_LISTS);
   if ((int64_t)p->top_k + p->window > 1152 * 64)
     return fail(HS_ERR_UNSUPPORTED, "selection capacity %d too large", p->top_k + p->window);
   SparsePlan pl;
@@ -642,7 +667,7 @@ hs_status hs_swa_attn(const hs_kv_cache* kv, const hs_attn_params* p, const void
   if (q_dtype != HS_BF16) return fail(HS_ERR_UNSUPPORTED, "q dtype must be BF16");
   if (kv->dtype == HS_F32) return fail(HS_ERR_UNSUPPORTED, "F32 caches are not supported here");
   if (!aligned16(q) || !aligned16(out)) return fail(HS_ERR_INVALID_ARGUMENT, "q/out not 16-byte aligned");
-  if ((int64_t)kv->batch * ci.n_kv > 65535) return fail(HS_ERR_UNSUPPORTED, "batch * num_kv_heads > 65535");
+  if ((int64_t)kv->batch * ci.n_kv > MAX_LISTS) return fail(HS_ERR_UNSUPPORTED, "batch * num_kv_heads > 65535");
   hs::AttnArgs a{};
   a.k = kv->k; a.v = kv->v; a.k_scale = kv->k_scale; a.v_scale = kv->v_scale;
   a.row_start = kv->d_row_start; a.seq_len = kv->d_seq_len;
@@ -673,6 +698,11 @@ hs_status hs_select_from_scores(const float* scores, const int32_t* d_seq_len, c
       return fail(HS_ERR_INVALID_ARGUMENT, "seq_len[%d] = %d outside [1, max_len]", b, h_seq_len[b]);
   if (select_block != 0 && select_block != 1 && select_block != 64)
     return fail(HS_ERR_UNSUPPORTED, "select_block %d (0, 1 or 64)", select_block);
+  if (!aligned4(scores) || !aligned4(sel_idx) || !aligned4(sel_count))
+    return fail(HS_ERR_INVALID_ARGUMENT, "scores/sel_idx/sel_count not 4-byte aligned");
+  if ((int64_t)batch * q_tokens * n_kv > MAX_LISTS)
+    return fail(HS_ERR_UNSUPPORTED, "batch * q_tokens * n_kv = %lld selection lists (at most %lld)",
+                (long long)batch * q_tokens * n_kv, (long long)MAX_LISTS);
   hs_status bst = check_block_select(select_block, max_len - std::min(window, max_len));
   if (bst != HS_OK) return bst;
   const size_t need = hs_select_workspace_size(batch, q_tokens, n_kv, max_len, top_k, window);

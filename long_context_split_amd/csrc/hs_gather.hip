@@ -90,7 +90,9 @@ __global__ __launch_bounds__(64 * NW) void attn_gather_kernel(AttnArgs a) {
   }
   const int Lb = a.seq_len[b];
   const int ntok = min(max(a.sel_count[(size_t)list], 0), a.sel_cap);
-  if (c0 >= ntok) return;                           // whole workgroup: the merge skips this chunk
+  // whole workgroup: the merge skips this chunk; a direct workgroup (the whole list) goes on with no
+  // tile, so an empty list gets zeros, as the merge writes for it
+  if (c0 >= ntok && !a.direct) return;
   const int c1 = min(ntok, c0 + a.chunk);
   const int ntiles = (c1 - c0 + 31) / 32;
   const int64_t rs = a.row_start[b];

@@ -40,8 +40,11 @@ CONFIGS = {
             n_sparse=5, n_blocks=4, kv="bf16", q="bf16", needles=0),
 }
 
-# Aligned-cluster strength for config 3 (key = alpha * sqrt(d) * unit query).
-C3_ALPHA = 0.5
+# Aligned-cluster strengths for config 3 (key = alpha * sqrt(d) * unit query), one per
+# aligned cluster: (t=0, h=0) and (t=1, h=1).  Tuned so that, with the oracle's scores on
+# the stored E4M3 keys at L = 1,048,576, the 1024-th global score of query token t falls
+# inside cluster t: part of each cluster is selected and part is not.
+C3_ALPHA = (0.4285, 0.4608)
 
 
 def rng(cfg, tensor, sub=0):
@@ -177,6 +180,19 @@ def decode_case(cfg, L=None, B=None, seqs=None, block=0, lengths=None):
                 q_sparse=q_sparse, k=k_out, v=v_out, needles=needles)
 
 
+def _cluster_draw(cfg, spec, b, L):
+    g = rng(cfg, T_CLUSTER, b)
+    n = int(round(spec["cluster_frac"] * L))
+    pos = g.choice(L - WINDOW, size=n, replace=False)
+    return g, np.array_split(pos, spec["n_clusters"])
+
+
+def cluster_positions(cfg, b, L):
+    """Row positions of each near-duplicate cluster of sequence b (cluster 0 is aligned with
+    query (t=0, h=0), cluster 1 with (t=1, h=1)), as decode_case plants them."""
+    return _cluster_draw(cfg, CONFIGS[cfg], b, int(L))[1]
+
+
 def _plant_clusters(cfg, spec, b, k_rows, q_f32, L):
     """Config 3's near-duplicate key clusters (1% of rows, 16 clusters).
 
@@ -184,14 +200,11 @@ def _plant_clusters(cfg, spec, b, k_rows, q_f32, L):
     of (t=1, h=1), so that many near-identical keys compete at the top-k
     boundary; the other centres are standard normal vectors.
     """
-    g = rng(cfg, T_CLUSTER, b)
-    n = int(round(spec["cluster_frac"] * L))
-    pos = g.choice(L - WINDOW, size=n, replace=False)
-    groups = np.array_split(pos, spec["n_clusters"])
+    g, groups = _cluster_draw(cfg, spec, b, L)
     centers = g.standard_normal((spec["n_clusters"], HEAD_DIM), dtype=np.float32)
     for ci, (t, h) in enumerate([(0, 0), (1, 1)]):
         qv = q_f32[t, h].astype(np.float64)
-        centers[ci] = (C3_ALPHA * np.sqrt(HEAD_DIM) * qv / np.linalg.norm(qv)).astype(np.float32)
+        centers[ci] = (C3_ALPHA[ci] * np.sqrt(HEAD_DIM) * qv / np.linalg.norm(qv)).astype(np.float32)
     for ci, grp in enumerate(groups):
         noise = g.standard_normal((len(grp), HEAD_DIM), dtype=np.float32)
         k_rows[grp, 0, :] = centers[ci][None, :] + np.float32(1e-3) * noise

@@ -73,12 +73,21 @@ class Uploaded:
         return q, k, v
 
 
-def recall(gpu_idx, gpu_cnt, ref_idx, ref_cnt, L, top_k, window):
-    """Global-part recall |G_gpu & G_ref| / |G_ref| over one list (window excluded)."""
+def recall(gpu_idx, gpu_cnt, ref_idx, ref_cnt, L, top_k, window, ref_scores=None):
+    """Global-part recall of one list (window excluded): (|G_gpu & G_ref|, |G_ref|, tie-aware hits).
+
+    Tie-aware hits count a GPU-selected j as correct when the oracle's score of j reaches the
+    oracle's k'-th score times (1 - 1e-6), so swaps among near-tied scores at the boundary are
+    not counted as misses (equal to the plain hits when ref_scores is None)."""
     kk = max(0, min(top_k, L - window))
     g = set(gpu_idx[:kk].tolist())
     r = set(ref_idx[:kk].tolist())
-    return len(g & r), len(r)
+    hit = len(g & r)
+    tie = hit
+    if ref_scores is not None and kk > 0:
+        kth = np.min(ref_scores[ref_idx[:kk]])
+        tie = sum(1 for j in g if ref_scores[j] >= kth * (1.0 - 1e-6))
+    return hit, len(r), tie
 
 
 def f32_scores_view(scores_dev, b, t, g, n):

@@ -176,3 +176,48 @@ def test_append_rejects(hs):
     assert f(0x900000, 2, 4096, 1, w, w, tp, 0xA00000, p, 0xB00000, need - 16, None) == 3   # workspace too small
     assert f(0x900000, 2, 4096, 1, w, w, tp, 0xA00000, p, None, 0, None) == 1          # no workspace
     assert f(0x900000, 0, 4096, 1, w, w, tp, None, None, None, 0, None) == 0           # nothing to do: no launch
+
+
+def test_workspace_size_per_query_type(hs):
+    """A bf16 plan exists up to 256 heads per KV head, an fp32 one up to 128: the size query answers
+    with the largest plan that exists and leaves the caller's last error alone."""
+    c = _cache(hs)
+    assert _call_full(hs, c, hs.params(31, 1)) == 2                   # sets a last error
+    before = hs.last_error()
+    assert before
+    for H in (32, 128, 256):
+        assert hs.lib.hs_full_attn_select_workspace_size(ctypes.byref(c), ctypes.byref(hs.params(H, 1))) > 0, H
+    assert hs.lib.hs_full_attn_select_workspace_size(ctypes.byref(c), ctypes.byref(hs.params(160, 1))) == 0
+    assert hs.lib.hs_full_attn_select_workspace_size(ctypes.byref(c), ctypes.byref(hs.params(512, 1))) == 0
+    assert hs.last_error() == before
+    # a G = 256 bf16 call with that workspace passes validation up to the launch (no device here:
+    # a too-small workspace is the last check before it)
+    need = hs.lib.hs_full_attn_select_workspace_size(ctypes.byref(c), ctypes.byref(hs.params(256, 1)))
+    assert _call_full(hs, c, hs.params(256, 1), nbytes=need - 1) == 3
+    assert _call_full(hs, c, hs.params(256, 1), q_dtype=0, nbytes=need) == 2   # fp32 queries: G <= 128
+    assert _call_full(hs, c, hs.params(96, 1)) == 2                   # not a power of two
+
+
+def test_output_alignment_and_list_limit(hs):
+    c = _cache(hs)
+    p = hs.params(32, 1)
+    f = hs.lib.hs_full_attn_select
+
+    def call(out=0x400000, lse=None, idx=0x500000, cnt=0x600000, sc=None, cache=c, prm=p):
+        return f(ctypes.byref(cache), ctypes.byref(prm), 0x200000, 1, out, lse, idx, cnt, sc, 0x300000, 1 << 40, None)
+
+    assert call(out=0x400008) == 1                                   # out: float4 stores
+    assert call(lse=0x400002) == 1
+    assert call(idx=0x500002) == 1
+    assert call(cnt=0x600001) == 1
+    assert call(sc=0x700002) == 1
+    many = _cache(hs, lens=[1] * 70000, cap=70000)                   # more lists than a grid dimension holds
+    assert call(cache=many) == 2
+    assert "lists" in hs.last_error()
+    s = hs.lib.hs_sparse_attn
+    assert s(ctypes.byref(c), ctypes.byref(p), 0x200000, 1, 0x500000, 0x600000, 0x400008, 0x300000, 1 << 40,
+             None) == 1
+    assert s(ctypes.byref(c), ctypes.byref(p), 0x200000, 1, 0x500002, 0x600000, 0x400000, 0x300000, 1 << 40,
+             None) == 1
+    assert s(ctypes.byref(many), ctypes.byref(p), 0x200000, 1, 0x500000, 0x600000, 0x400000, 0x300000, 1 << 40,
+             None) == 2
