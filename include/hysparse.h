@@ -230,6 +230,26 @@ hs_status hs_sparse_attn(const hs_kv_cache *kv, const hs_attn_params *p, const v
                          hs_dtype q_dtype, const int32_t *sel_idx, const int32_t *sel_count,
                          float *out, void *workspace, size_t workspace_bytes, void *stream);
 
+/* hs_sparse_attn without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments (minus the workspace), same
+ * launches and the same results as hs_sparse_attn.  Its scratch (the per-chunk
+ * partials of the sparse layer) is a static device array of
+ * HS_NOALLOC_SCRATCH_BYTES (8 MiB) that every GPU the library runs on holds
+ * until the process ends; the call allocates nothing.  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (on different
+ * streams, or from different host threads) race on it and must not be issued.
+ * Nothing in it needs clearing between calls.  `stream` (NULL: the null stream)
+ * must belong to the calling thread's current device.  Errors: as
+ * hs_sparse_attn (no workspace errors), HS_ERR_INVALID_ARGUMENT for a stream of
+ * another device, and HS_ERR_UNSUPPORTED when the shapes need more scratch than
+ * the array holds (hs_sparse_attn_workspace_size() bounds what they need; lists
+ * that fit one workgroup each need none). */
+#define HS_NOALLOC_SCRATCH_BYTES (8u << 20)
+hs_status hs_sparse_attn_noalloc(const hs_kv_cache *kv, const hs_attn_params *p, const void *q,
+                                 hs_dtype q_dtype, const int32_t *sel_idx, const int32_t *sel_count,
+                                 float *out, void *stream);
+
 /* Sliding-window attention of the Self-Decoder side, which feeds KV Bridging
  * (ithome page, architecture overview: the Self-Decoder mixes full and
  * sliding-window attention over the current input; the pages give no window

@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -366,6 +367,48 @@ hs_status bridge_args(const void* hidden, int64_t n_tokens, int32_t d_model, int
   return HS_OK;
 }
 
+// ---------------------------------------------------------------- static scratch of hs_sparse_attn_noalloc
+
+// The sparse layer's chunk partials for callers that cannot allocate: one array per GPU, loaded with
+// the library's code object and kept until the process ends.  Host code never uses the array's name
+// as an address (on the host it is only a stand-in): the device address of each GPU's copy is looked
+// up once, with that device current, and kept here.
+__device__ __align__(256) static char scratch[HS_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES];
+
+// Device address of the current device's scratch array; the stream (null: the current device's null
+// stream) must belong to that device.
+hs_status scratch_for_stream(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(HS_ERR_UNSUPPORTED, "device %d (at most %d devices)", dev, MAX_DEVICES);
+  if (stream) {
+    int sdev = -1;
+    if ((e = hipStreamGetDevice(stream, &sdev)) != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+    if (sdev != dev)
+      return fail(HS_ERR_INVALID_ARGUMENT, "stream of device %d while device %d is current", sdev, dev);
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess)
+      return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(HS_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return HS_OK;
+}
+
+// hs_sparse_attn with its scratch either from the caller's workspace or (noalloc) from the static array.
+hs_status sparse_attn_impl(const hs_kv_cache* kv, const hs_attn_params* p, const void* q, hs_dtype q_dtype,
+                           const int32_t* sel_idx, const int32_t* sel_count, float* out, void* workspace,
+                           size_t workspace_bytes, bool noalloc, void* stream);
+
 }  // namespace
 
 extern "C" {
@@ -592,58 +635,13 @@ hs_status hs_sparse_attn(const hs_kv_cache* kv, const hs_attn_params* p, const v
                          const int32_t* sel_idx, const int32_t* sel_count, float* out, void* workspace,
                          size_t workspace_bytes, void* stream) {
   g_last_error.clear();
-  CacheInfo ci;
-  hs_status st = check_cache(kv, ci, true);
-  if (st != HS_OK) return st;
-  if ((st = check_params(p, ci.n_kv)) != HS_OK) return st;
-  if (!q || !out || !sel_idx || !sel_count) return fail(HS_ERR_INVALID_ARGUMENT, "q/out/sel_idx/sel_count is NULL");
-  if (q_dtype != HS_F32 && q_dtype != HS_BF16) return fail(HS_ERR_INVALID_ARGUMENT, "q dtype must be F32 or BF16");
-  if (!aligned16(q)) return fail(HS_ERR_INVALID_ARGUMENT, "q not 16-byte aligned");
-  if (!aligned16(out)) return fail(HS_ERR_INVALID_ARGUMENT, "out not 16-byte aligned");
-  if (!aligned4(sel_idx) || !aligned4(sel_count))
-    return fail(HS_ERR_INVALID_ARGUMENT, "sel_idx/sel_count not 4-byte aligned");
-  if ((int64_t)ci.B * p->q_tokens * ci.n_kv > MAX_LISTS)
-    return fail(HS_ERR_UNSUPPORTED, "batch * q_tokens * num_kv_heads = %lld selection lists (at most %lld)",
-                (long long)ci.B * p->q_tokens * ci.n_kv, (long long)MAX_LISTS);
-  if ((int64_t)p->top_k + p->window > 1152 * 64)
-    return fail(HS_ERR_UNSUPPORTED, "selection capacity %d too large", p->top_k + p->window);
-  SparsePlan pl;
-  plan_sparse(kv, p, q_dtype, ci, pl);
-  if (!workspace && pl.total) return fail(HS_ERR_INVALID_ARGUMENT, "workspace is NULL");
-  if (workspace_bytes < pl.total)
-    return fail(HS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, pl.total);
-  if (!aligned16(workspace)) return fail(HS_ERR_INVALID_ARGUMENT, "workspace not 16-byte aligned");
+  return sparse_attn_impl(kv, p, q, q_dtype, sel_idx, sel_count, out, workspace, workspace_bytes, false, stream);
+}
 
-  hipStream_t s = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  hs::AttnArgs a{};
-  a.k = kv->k; a.v = kv->v; a.k_scale = kv->k_scale; a.v_scale = kv->v_scale;
-  a.row_start = kv->d_row_start; a.seq_len = kv->d_seq_len;
-  a.q = q; a.q_f32 = q_dtype == HS_F32;
-  a.n_kv = ci.n_kv; a.H = p->num_q_heads; a.G = pl.G; a.n_q = p->q_tokens;
-  a.R = pl.G; a.n_lists = pl.n_lists; a.chunk = pl.chunk; a.max_chunks = pl.max_chunks;
-  a.scale_log2 = scale_log2(p);
-  a.sel_idx = sel_idx; a.sel_count = sel_count; a.sel_cap = pl.cap;
-  a.part_acc = (float*)(ws + pl.off_acc); a.part_ml = (float*)(ws + pl.off_ml);
-  if (pl.gather) {
-    a.direct = pl.max_chunks == 1; a.out = out; a.lse = nullptr; a.lse2 = nullptr;
-    hipError_t e = timed("attn_gather", s, [&] { return hs::launch_attn_gather(a, kv_type(kv->dtype), s); });
-    if (e != hipSuccess) return hip_fail(e, "sparse attention");
-    if (a.direct) return HS_OK;
-  }
-  hipError_t e = hipSuccess;
-  if (!pl.gather) {
-    e = timed("attn_partial_gather", s, [&] { return hs::launch_attn_partial(a, kv_type(kv->dtype), pl.ct, pl.nwr, true, s); });
-    if (e != hipSuccess) return hip_fail(e, "sparse attention");
-  }
-  hs::MergeArgs m{};
-  m.part_acc = a.part_acc; m.part_ml = a.part_ml; m.seq_len = kv->d_seq_len; m.sel_count = sel_count;
-  m.sel_cap = pl.cap;
-  m.gather = 1; m.n_kv = ci.n_kv; m.H = a.H; m.G = pl.G; m.n_q = a.n_q; m.R = pl.G; m.n_lists = pl.n_lists;
-  m.chunk = pl.chunk; m.max_chunks = pl.max_chunks; m.out = out; m.lse = nullptr; m.lse2 = nullptr;
-  if ((e = timed("attn_merge_gather", s, [&] { return hs::launch_attn_merge(m, s); })) != hipSuccess)
-    return hip_fail(e, "sparse attention merge");
-  return HS_OK;
+hs_status hs_sparse_attn_noalloc(const hs_kv_cache* kv, const hs_attn_params* p, const void* q, hs_dtype q_dtype,
+                                 const int32_t* sel_idx, const int32_t* sel_count, float* out, void* stream) {
+  g_last_error.clear();
+  return sparse_attn_impl(kv, p, q, q_dtype, sel_idx, sel_count, out, nullptr, 0, true, stream);
 }
 
 hs_status hs_swa_attn(const hs_kv_cache* kv, const hs_attn_params* p, const void* q, hs_dtype q_dtype,
@@ -797,3 +795,75 @@ hs_status hs_kv_append(const void* hidden, int64_t n_tokens, int32_t d_model, in
 }
 
 }  // extern "C"
+
+namespace {
+
+hs_status sparse_attn_impl(const hs_kv_cache* kv, const hs_attn_params* p, const void* q, hs_dtype q_dtype,
+                           const int32_t* sel_idx, const int32_t* sel_count, float* out, void* workspace,
+                           size_t workspace_bytes, bool noalloc, void* stream) {
+  CacheInfo ci;
+  hs_status st = check_cache(kv, ci, true);
+  if (st != HS_OK) return st;
+  if ((st = check_params(p, ci.n_kv)) != HS_OK) return st;
+  if (!q || !out || !sel_idx || !sel_count) return fail(HS_ERR_INVALID_ARGUMENT, "q/out/sel_idx/sel_count is NULL");
+  if (q_dtype != HS_F32 && q_dtype != HS_BF16) return fail(HS_ERR_INVALID_ARGUMENT, "q dtype must be F32 or BF16");
+  if (!aligned16(q)) return fail(HS_ERR_INVALID_ARGUMENT, "q not 16-byte aligned");
+  if (!aligned16(out)) return fail(HS_ERR_INVALID_ARGUMENT, "out not 16-byte aligned");
+  if (!aligned4(sel_idx) || !aligned4(sel_count))
+    return fail(HS_ERR_INVALID_ARGUMENT, "sel_idx/sel_count not 4-byte aligned");
+  if ((int64_t)ci.B * p->q_tokens * ci.n_kv > MAX_LISTS)
+    return fail(HS_ERR_UNSUPPORTED, "batch * q_tokens * num_kv_heads = %lld selection lists (at most %lld)",
+                (long long)ci.B * p->q_tokens * ci.n_kv, (long long)MAX_LISTS);
+  if ((int64_t)p->top_k + p->window > 1152 * 64)
+    return fail(HS_ERR_UNSUPPORTED, "selection capacity %d too large", p->top_k + p->window);
+  SparsePlan pl;
+  plan_sparse(kv, p, q_dtype, ci, pl);
+  if (noalloc) {
+    // the partials go to the static array; one workgroup per list (attn_gather's direct form) needs none
+    const size_t need = (pl.gather && pl.max_chunks == 1) ? 0 : pl.total;
+    if (need > HS_NOALLOC_SCRATCH_BYTES)
+      return fail(HS_ERR_UNSUPPORTED, "these shapes need %zu bytes of scratch, more than the %zu-byte static "
+                  "array of hs_sparse_attn_noalloc (use hs_sparse_attn with a workspace)", need,
+                  (size_t)HS_NOALLOC_SCRATCH_BYTES);
+    hs_status sst = scratch_for_stream((hipStream_t)stream, &workspace);
+    if (sst != HS_OK) return sst;
+    workspace_bytes = HS_NOALLOC_SCRATCH_BYTES;
+  }
+  if (!workspace && pl.total) return fail(HS_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (workspace_bytes < pl.total && !noalloc)
+    return fail(HS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, pl.total);
+  if (!aligned16(workspace)) return fail(HS_ERR_INVALID_ARGUMENT, "workspace not 16-byte aligned");
+
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  hs::AttnArgs a{};
+  a.k = kv->k; a.v = kv->v; a.k_scale = kv->k_scale; a.v_scale = kv->v_scale;
+  a.row_start = kv->d_row_start; a.seq_len = kv->d_seq_len;
+  a.q = q; a.q_f32 = q_dtype == HS_F32;
+  a.n_kv = ci.n_kv; a.H = p->num_q_heads; a.G = pl.G; a.n_q = p->q_tokens;
+  a.R = pl.G; a.n_lists = pl.n_lists; a.chunk = pl.chunk; a.max_chunks = pl.max_chunks;
+  a.scale_log2 = scale_log2(p);
+  a.sel_idx = sel_idx; a.sel_count = sel_count; a.sel_cap = pl.cap;
+  a.part_acc = (float*)(ws + pl.off_acc); a.part_ml = (float*)(ws + pl.off_ml);
+  if (pl.gather) {
+    a.direct = pl.max_chunks == 1; a.out = out; a.lse = nullptr; a.lse2 = nullptr;
+    hipError_t e = timed("attn_gather", s, [&] { return hs::launch_attn_gather(a, kv_type(kv->dtype), s); });
+    if (e != hipSuccess) return hip_fail(e, "sparse attention");
+    if (a.direct) return HS_OK;
+  }
+  hipError_t e = hipSuccess;
+  if (!pl.gather) {
+    e = timed("attn_partial_gather", s, [&] { return hs::launch_attn_partial(a, kv_type(kv->dtype), pl.ct, pl.nwr, true, s); });
+    if (e != hipSuccess) return hip_fail(e, "sparse attention");
+  }
+  hs::MergeArgs m{};
+  m.part_acc = a.part_acc; m.part_ml = a.part_ml; m.seq_len = kv->d_seq_len; m.sel_count = sel_count;
+  m.sel_cap = pl.cap;
+  m.gather = 1; m.n_kv = ci.n_kv; m.H = a.H; m.G = pl.G; m.n_q = a.n_q; m.R = pl.G; m.n_lists = pl.n_lists;
+  m.chunk = pl.chunk; m.max_chunks = pl.max_chunks; m.out = out; m.lse = nullptr; m.lse2 = nullptr;
+  if ((e = timed("attn_merge_gather", s, [&] { return hs::launch_attn_merge(m, s); })) != hipSuccess)
+    return hip_fail(e, "sparse attention merge");
+  return HS_OK;
+}
+
+}  // namespace

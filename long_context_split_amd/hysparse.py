@@ -82,6 +82,8 @@ lib.hs_full_attn_select.restype = ctypes.c_int
 lib.hs_full_attn_select.argtypes = [_KVP, _PP, _P, ctypes.c_int, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
 lib.hs_sparse_attn.restype = ctypes.c_int
 lib.hs_sparse_attn.argtypes = [_KVP, _PP, _P, ctypes.c_int, _P, _P, _P, _P, ctypes.c_size_t, _P]
+lib.hs_sparse_attn_noalloc.restype = ctypes.c_int
+lib.hs_sparse_attn_noalloc.argtypes = [_KVP, _PP, _P, ctypes.c_int, _P, _P, _P, _P]
 lib.hs_swa_attn.restype = ctypes.c_int
 lib.hs_swa_attn.argtypes = [_KVP, _PP, _P, ctypes.c_int, _P, _P]
 lib.hs_select_from_scores.restype = ctypes.c_int
@@ -258,6 +260,19 @@ def sparse_attn(kv, q, sel_idx, sel_count, top_k=1024, window=128, softmax_scale
         ws = workspace(sparse_attn_workspace_size(kv, p), dev)
     check(lib.hs_sparse_attn(kv.c, ctypes.byref(p), _ptr(q), query_dtype(q), _ptr(sel_idx), _ptr(sel_count),
                              _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def sparse_attn_noalloc(kv, q, sel_idx, sel_count, top_k=1024, window=128, softmax_scale=0.0, out=None,
+                        stream=None):
+    """hs_sparse_attn_noalloc: the sparse layer with its scratch in the library's static device array
+    (no workspace).  out must be given by callers that cannot allocate."""
+    B, n_q, H, d = q.shape
+    p = params(H, n_q, top_k, window, softmax_scale)
+    if out is None:
+        out = torch.empty((B, n_q, H, d), dtype=torch.float32, device=q.device)
+    check(lib.hs_sparse_attn_noalloc(kv.c, ctypes.byref(p), _ptr(q), query_dtype(q), _ptr(sel_idx),
+                                     _ptr(sel_count), _ptr(out), _stream(stream)))
     return out
 
 

@@ -221,3 +221,17 @@ def test_output_alignment_and_list_limit(hs):
              None) == 1
     assert s(ctypes.byref(many), ctypes.byref(p), 0x200000, 1, 0x500000, 0x600000, 0x400000, 0x300000, 1 << 40,
              None) == 2
+
+
+def test_sparse_attn_noalloc_rejects_before_launch(hs):
+    """The no-workspace sparse layer validates like hs_sparse_attn, and refuses shapes whose
+    partials exceed its static array, all before touching a device."""
+    f = hs.lib.hs_sparse_attn_noalloc
+    c = _cache(hs)
+    p = hs.params(32, 1)
+    assert f(ctypes.byref(c), ctypes.byref(p), 0x200000, 1, None, 0x500000, 0x400000, None) == 1
+    assert f(ctypes.byref(c), ctypes.byref(p), 0x200000, 1, 0x500000, 0x600000, 0x400008, None) == 1
+    big = _cache(hs, dtype=0, lens=[1200] * 4096, cap=1200 * 4096)
+    pb = hs.params(128, 1)
+    assert f(ctypes.byref(big), ctypes.byref(pb), 0x200000, 0, 0x500000, 0x600000, 0x400000, None) == 2
+    assert "static" in hs.last_error()
