@@ -169,7 +169,13 @@ struct FullPlan {
   // hs::cand_nper of its candidate count), each filling its own region of cand_region pairs
   int cand, cand_wgs, cand_uniform;
   int64_t cand_region, cand_total;
-  size_t off_acc, off_ml, off_lse2, off_scores, off_sel, total;
+  // score filter (one query token, wave path, no dense scores asked for): the dense pass writes
+  // per-(token, row) codes, the bounds pass keeps upper-bound digits and a lower-bound histogram per
+  // list, the exact pass recomputes only the tokens that can reach the k'-th score (cand_wgs
+  // workgroups as in candidate mode, regions of f_region pairs)
+  int filter, f_chunk;
+  int64_t code_tiles, u_stride, f_region;
+  size_t off_acc, off_ml, off_lse2, off_scores, off_sel, off_codes, off_udig, off_lhist, total;
   hs::SelectPlan sel;
 };
 
@@ -263,12 +269,15 @@ hs_status plan_full(const hs_kv_cache* kv, const hs_attn_params* p, hs_dtype q_d
   pl.cand = pl.wave && p->q_tokens == 1 && p->select_block == 0 && pl.n_lists >= cand_min_lists &&
             (equal_len || pl.n_lists <= 64) && pl.s_stride <= hs::SELECT_CAND_MAX_N &&
             !env_int("HS_DENSE_SELECT", 0);
+  pl.filter = pl.wave && p->q_tokens == 1 && p->select_block == 0 && pl.s_stride <= hs::SELECT_CAND_MAX_N &&
+              !env_int("HS_DENSE_SELECT", 0) && env_int("HS_SCORE_FILTER", 1) != 0;
   pl.cand_wgs = 0;
   pl.cand_region = 0;
   pl.cand_uniform = equal_len;
   pl.cand_total = 0;
+  pl.f_region = 0;
   int64_t cand_pairs = 0;
-  if (pl.cand) {
+  if (pl.cand || pl.filter) {
     for (int l = 0; l < pl.n_lists; ++l) {
       const int64_t L = kv->h_seq_len[l / ci.n_kv];
       pl.cand_total += L - std::min<int64_t>(p->window, L);
@@ -279,13 +288,28 @@ hs_status plan_full(const hs_kv_cache* kv, const hs_attn_params* p, hs_dtype q_d
       const int np = hs::cand_nper(nc, pl.cand_total);
       pl.cand_wgs += np;
       max_nper = std::max(max_nper, np);
-      pl.cand_region = std::max(pl.cand_region, hs::scores_cand_region(nc, np));
+      if (pl.cand) pl.cand_region = std::max(pl.cand_region, hs::scores_cand_region(nc, np));
+      if (pl.filter)   // the exact pass: a workgroup's token range, each token at most one pair
+        pl.f_region = std::max<int64_t>(pl.f_region, align_up((size_t)((nc + np - 1) / np), hs::FILTER_SPAN_ALIGN));
     }
-    cand_pairs = pl.cand_region * max_nper;
+    cand_pairs = std::max(pl.cand_region, pl.f_region) * max_nper;
   }
   hs::select_plan(pl.s_stride, pl.sel, cand_pairs);
   pl.off_sel = off;
   off += align_up((size_t)ci.B * p->q_tokens * ci.n_kv * pl.sel.ws_stride * 4, 256);
+  pl.code_tiles = (ci.maxL + 31) / 32;
+  pl.u_stride = (int64_t)align_up((size_t)std::max<int64_t>(pl.s_stride, 1), 32);
+  pl.f_chunk = (int)align_up((size_t)std::max<int64_t>(hs::FILTER_BOUNDS_CHUNK, (pl.cand_total + 511) / 512),
+                             hs::FILTER_BOUNDS_CHUNK);
+  pl.off_codes = pl.off_udig = pl.off_lhist = 0;
+  if (pl.filter) {
+    pl.off_codes = off;
+    off += align_up((size_t)pl.n_lists * pl.code_tiles * hs::CODE_TILE_BYTES, 256);
+    pl.off_udig = off;
+    off += align_up((size_t)pl.n_lists * pl.u_stride * 2, 256);
+    pl.off_lhist = off;
+    off += align_up((size_t)pl.n_lists * 2048 * 4, 256);
+  }
   pl.total = off;
   return HS_OK;
 }
@@ -537,6 +561,15 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
     a.zero_words = hs::SELECT_ZERO_WORDS;
     a.zero_lists = n_sel_lists;
   }
+  // score filter when no dense scores are asked for: the dense pass leaves its codes and clears the
+  // lower-bound histograms
+  const bool use_filter = pl.filter && !scores_out;
+  if (use_filter) {
+    a.codes = (uint8_t*)(ws + pl.off_codes);
+    a.code_tiles = pl.code_tiles;
+    a.zero2_ptr = (uint32_t*)(ws + pl.off_lhist);
+    a.zero2_words = (int64_t)pl.n_lists * 2048;
+  }
   // items of the one-dimensional grids: chunks with work per list (lists in order)
   // (and the per-list count when it is the same for every list, which spares the kernel the search)
   auto count_items = [&](int chunk, int sub, int min_items, int& uniform) {
@@ -573,7 +606,28 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
     if ((e = timed("attn_merge_dense", s, [&] { return hs::launch_attn_merge(m, s); })) != hipSuccess)
       return hip_fail(e, "full attention merge");
 
-  if (pl.max_chunks_s > 0 || fold_merge) {
+  if (use_filter) {
+    hs::FilterArgs fa{};
+    fa.k = kv->k; fa.k_scale = kv->k_scale; fa.row_start = kv->d_row_start; fa.seq_len = kv->d_seq_len;
+    fa.q = q; fa.q_f32 = a.q_f32; fa.n_kv = ci.n_kv; fa.H = a.H; fa.G = pl.G; fa.R = pl.R; fa.n_lists = pl.n_lists;
+    fa.window = p->window; fa.top_k = p->top_k; fa.scale_log2 = sl2;
+    fa.codes = a.codes; fa.code_tiles = pl.code_tiles;
+    fa.udig = (uint16_t*)(ws + pl.off_udig); fa.u_stride = pl.u_stride;
+    fa.lhist = (uint32_t*)(ws + pl.off_lhist); fa.lse2 = lse2;
+    fa.chunk = pl.f_chunk;
+    fa.n_items = count_items(pl.f_chunk, p->window, 1, fa.uniform_items);
+    if (fold_merge) {
+      fa.part_acc = a.part_acc; fa.part_ml = a.part_ml; fa.dchunk = pl.chunk; fa.dmax_chunks = pl.max_chunks;
+      fa.out = out; fa.lse = lse;
+    }
+    fa.sel_ws = (uint32_t*)(ws + pl.off_sel); fa.sel_stride = pl.sel.ws_stride; fa.cand_off = pl.sel.cand_off;
+    fa.cand_region = pl.f_region; fa.cand_total = pl.cand_total; fa.cand_uniform = pl.cand_uniform;
+    fa.n_wg2 = pl.cand_wgs;
+    if ((e = timed("filter_bounds", s, [&] { return hs::launch_filter_bounds(fa, s); })) != hipSuccess)
+      return hip_fail(e, "score filter bounds");
+    if ((e = timed("filter_exact", s, [&] { return hs::launch_filter_exact(fa, kvt, s); })) != hipSuccess)
+      return hip_fail(e, "score filter exact scores");
+  } else if (pl.max_chunks_s > 0 || fold_merge) {
     hs::ScoreArgs sa{};
     sa.k = kv->k; sa.k_scale = kv->k_scale; sa.row_start = kv->d_row_start; sa.seq_len = kv->d_seq_len;
     sa.q = q; sa.q_f32 = a.q_f32; sa.n_kv = ci.n_kv; sa.H = a.H; sa.G = pl.G; sa.n_q = a.n_q; sa.R = pl.R;
@@ -620,10 +674,10 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
   se.sel_idx = sel_idx; se.sel_count = sel_count;
   se.ws = (uint32_t*)(ws + pl.off_sel); se.ws_stride = pl.sel.ws_stride; se.cand_off = pl.sel.cand_off;
   se.chunk = pl.sel.chunk; se.max_chunks = pl.sel.max_chunks;
-  se.cand_region = pl.cand_region;                               // region count per list: from the score pass
+  se.cand_region = use_filter ? pl.f_region : pl.cand_region;   // region count per list: from the score pass
   if (p->select_block == 64)
     e = timed("select_blocks", s, [&] { return hs::launch_select_blocks(se, n_sel_lists, pl.s_stride, s); });
-  else if (cand_mode)
+  else if (cand_mode || use_filter)
     e = timed("select_cand", s, [&] { return hs::launch_select_cand(se, n_sel_lists, s); });
   else
     e = timed("select_topk", s, [&] { return hs::launch_select(se, n_sel_lists, fused_prefix, s); });

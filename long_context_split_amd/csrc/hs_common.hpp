@@ -103,6 +103,35 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Selection scores of the 32-token S tile a wave holds (S = Q K^T from v_mfma_f32_32x32x16_bf16:
+// lane l has token l & 31 and the rows 8 (r / 4) + 4 (l >> 5) + (r & 3)): for each of the NQ query
+// tokens of the 32 rows (tpw tokens of G = 32 / tpw rows each, or one token when tpw = 1), the sum
+// over its rows of 2^(s f - lse2) in a fixed order.  f = softmax scale in log2 units (times the
+// token's K scale for E4M3), lse2 = the row's log-sum-exp in log2 units (+inf for padding rows).
+// Every pass that computes selection scores goes through here, so they agree bit for bit.
+template <int NQ>
+__device__ __forceinline__ void tile_scores(const f32x16& s, float f, const float (&lse2)[16], int tpw,
+                                            float (&tv)[NQ]) {
+  float p[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) p[r] = exp2_fast(fmaf(s[r], f, -lse2[r]));
+  if (tpw == 1) {
+    float v = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v += p[r];
+    tv[0] = v + __shfl_xor(v, 32);
+  } else {
+    float blk[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      blk[q4] = p[4 * q4] + p[4 * q4 + 1] + p[4 * q4 + 2] + p[4 * q4 + 3];
+      blk[q4] += __shfl_xor(blk[q4], 32);
+    }
+#pragma unroll
+    for (int t = 0; t < NQ; ++t) tv[t] = tpw == 4 ? blk[t] : blk[2 * t] + blk[2 * t + 1];
+  }
+}
+
 // Clears runs of words with the whole grid (any grid shape): `lists` runs of `words` words,
 // `stride` words apart.  No-op when ptr is null.
 __device__ __forceinline__ void zero_words_grid(uint32_t* ptr, int64_t stride, int words, int lists) {
@@ -231,6 +260,56 @@ __device__ inline float2 merged_o(const float* ml, size_t mstride, const float* 
     }
   }
   return o;
+}
+
+// The full layer's merge folded into a later pass over the same list (at most 64 dense chunks):
+// every workgroup of the list derives the LSE of all R rows from the chunk partials into s_lse2
+// (log2 units), and the rows r with r % nwg == cidx are merged by this workgroup: out (normalised),
+// lse (natural log) and lse2 (log2), the last two nullable.  The rows this workgroup merges and the
+// LSE table rows are loaded in one batch (lane = chunk), then reduced row by row.  Whole workgroup
+// of NW waves; s_lse2 is complete only after a barrier.
+template <int NW>
+__device__ void fold_merge(const float* part_acc, const float* part_ml, int dchunk, int dmax_chunks, int R, int G,
+                           int H, int n_q, int b, int g, int list, int Lb, int cidx, int nwg, float* s_lse2,
+                           float* out, float* lse, float* lse2, int wave, int lane) {
+  const int nchd = (Lb + dchunk - 1) / dchunk;                   // <= 64: one chunk per lane
+  const size_t first = (size_t)list * dmax_chunks * R;
+  constexpr int RPW = (32 + NW - 1) / NW;                        // rows per wave (R <= 32)
+  auto mrow = [&](int j) { return cidx + nwg * (wave + NW * j); };
+  float2 v[2 * RPW];
+#pragma unroll
+  for (int i = 0; i < 2 * RPW; ++i) {
+    const int r = min(i < RPW ? wave + NW * i : mrow(i - RPW), R - 1);
+    v[i] = *(const float2*)(part_ml + ((first + r) + (size_t)min(lane, nchd - 1) * R) * 2);
+    if (lane >= nchd) v[i] = make_float2(-INFINITY, 0.f);
+  }
+  float l2m[RPW];
+#pragma unroll
+  for (int i = 0; i < 2 * RPW; ++i) {
+    const int r = i < RPW ? wave + NW * i : mrow(i - RPW);
+    if (r >= R) continue;                                        // uniform over the wave
+    const float mx = wave_max(v[i].x);
+    const float ls = mx == -INFINITY ? 0.f : wave_sum(exp2f(v[i].x - mx) * v[i].y);
+    const float l2 = ls > 0.f ? mx + __log2f(ls) : -INFINITY;
+    if (i < RPW) {
+      if (lane == 0) s_lse2[r] = l2;
+    } else {
+      l2m[i - RPW] = l2;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) {
+    const int mr = mrow(j);
+    if (mr >= R) break;
+    const float* ml = part_ml + (first + mr) * 2;
+    const float2 o = l2m[j] == -INFINITY ? make_float2(0.f, 0.f)
+                                         : merged_o(ml, (size_t)R * 2, part_acc + (first + mr) * D,
+                                                    (size_t)R * D, 0, nchd, 1, l2m[j], lane);
+    const size_t orow = ((size_t)b * n_q + mr / G) * H + (size_t)g * G + mr % G;
+    *(float2*)(out + orow * D + 2 * lane) = o;
+    if (lane == 0 && lse) lse[orow] = l2m[j] * LN2;
+    if (lane == 0 && lse2) lse2[orow] = l2m[j];
+  }
 }
 
 }  // namespace hs

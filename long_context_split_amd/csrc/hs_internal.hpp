@@ -40,7 +40,19 @@ struct AttnArgs {
   int64_t zero_stride;   //   zero_lists runs of zero_words words, zero_stride apart
   int zero_words, zero_lists;
   int window;            // swa_attn: band width w (rows p - w + 1 .. p)
+  // attn_wave dense, optional (score filter): per 32-token tile of every list, a CODE_TILE_BYTES
+  // record at codes + (list * code_tiles + tile) * CODE_TILE_BYTES: 256 words [quad q][row h] whose
+  // byte i is the code of token 32 tile + 4 q + i and row h, code = floor(8 (l2 - m) + 191) clamped
+  // to [0, 255] with l2 the logit in log2 units and m the row's running reference in that tile, then
+  // the 32 references m (float, rows 0..31)
+  uint8_t* codes;
+  int64_t code_tiles;    // tiles per list (ceil(max L / 32))
+  uint32_t* zero2_ptr;   // attn_wave: a second run of words cleared by the grid (nullable)
+  int64_t zero2_words;
 };
+
+constexpr int CODE_TILE_BYTES = 1152;      // 1024 bytes of codes + 32 float references
+constexpr int CODE_OFFSET = 191;           // code = floor(8 x + CODE_OFFSET), x = l2 - m <= 8
 
 struct MergeArgs {
   const float* part_acc;
@@ -94,6 +106,46 @@ struct ScoreArgs {
   int cand_uniform;
   int64_t cand_total;    // sum over the lists of their candidate counts
 };
+
+// Score filter (one query token per list, at most 32 query rows per KV head, after attn_wave wrote
+// its codes): the bounds pass turns each candidate's codes into an upper and a lower bound of its
+// selection score, histograms the lower bounds per list and keeps the first digit of each upper
+// bound; the exact pass finds the highest digit d whose lower-bound bins hold k' tokens (so the
+// k'-th score is at least the smallest value of digit d), recomputes the exact score of every
+// token whose upper bound reaches that value, with the score pass's arithmetic, and appends the
+// (key, index) pairs and their first-digit histogram for the candidate-mode selection.
+struct FilterArgs {
+  const void* k;
+  const float* k_scale;
+  const int64_t* row_start;
+  const int32_t* seq_len;
+  const void* q;
+  int q_f32;
+  int n_kv, H, G, R, n_lists, window, top_k;
+  float scale_log2;
+  const uint8_t* codes;  // as AttnArgs::codes
+  int64_t code_tiles;
+  uint16_t* udig;        // [lists][u_stride] first digit (float bits >> 20) of each upper bound
+  int64_t u_stride;      //   a multiple of 32
+  uint32_t* lhist;       // [lists][2048] first-digit histogram of the lower bounds (cleared before)
+  float* lse2;           // [B, 1, H] log2 units: written by the bounds pass when it merges, else read
+  // bounds pass: one-dimensional grid of (list, chunk) items, chunk a multiple of 2048 tokens
+  int chunk, n_items, uniform_items;
+  const float* part_acc; // nullable: fold the full layer's merge (as scores_wave does)
+  const float* part_ml;
+  int dchunk, dmax_chunks;
+  float* out;
+  float* lse;            // nullable
+  // exact pass: cand_nper(ncand_l, cand_total) workgroups per list, consecutive; region `slot` of
+  // cand_region pairs at sel_ws + list * sel_stride + cand_off (words)
+  uint32_t* sel_ws;
+  int64_t sel_stride, cand_off, cand_region, cand_total;
+  int cand_uniform, n_wg2;
+};
+hipError_t launch_filter_bounds(const FilterArgs& a, hipStream_t st);
+hipError_t launch_filter_exact(const FilterArgs& a, int kvt, hipStream_t st);
+constexpr int FILTER_SPAN_ALIGN = 512;     // exact pass: token range of a workgroup, a multiple of this
+constexpr int FILTER_BOUNDS_CHUNK = 2048;  // bounds pass: chunk granule
 
 struct SelectArgs {
   const float* scores;   // [lists][s_stride]

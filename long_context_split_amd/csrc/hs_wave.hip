@@ -28,6 +28,7 @@ namespace {
 // Clears the words the caller asked for (the selection's histograms) with the whole grid.
 __device__ __forceinline__ void zero_hook(const AttnArgs& a) {
   zero_words_grid(a.zero_ptr, a.zero_stride, a.zero_words, a.zero_lists);
+  zero_words_grid(a.zero2_ptr, a.zero2_words, (int)a.zero2_words, 1);
 }
 
 // First digit of a score's key in candidate mode: key bits 30..20 (8 exponent and 3 fraction bits,
@@ -70,7 +71,10 @@ __device__ int lower_digit(const uint32_t* hist, uint32_t kk, int lane) {
 
 }  // namespace
 
-template <int KVT, int NW>
+// CODES: the score filter's codes are written (a.codes set).  A template parameter rather than a
+// branch: with the stores behind a branch the compiler cannot count them at the loop head, and each
+// tile would then wait for the previous tile's stores as well as for its own loads.
+template <int KVT, int NW, bool CODES>
 __global__ __launch_bounds__(64 * NW) void attn_wave_kernel(AttnArgs a) {
   constexpr int NT = 64 * NW;
   using M = Mma<CT_BF16>;
@@ -181,10 +185,24 @@ __global__ __launch_bounds__(64 * NW) void attn_wave_kernel(AttnArgs a) {
   float m = -INFINITY, lsum = 0.f;
   f32x16 acc[4] = {};
   const float sl2 = a.scale_log2;
+  // Score filter: a tile's codes are held in registers and stored during the wave's next tile, just
+  // before that tile's prefetch, so waiting for a prefetch never waits for younger stores.
+  uint32_t hw[4] = {0u, 0u, 0u, 0u};
+  float hm = 0.f;
+  int htile = -1;
+  auto put_codes = [&]() {
+    uint32_t* rec = (uint32_t*)(a.codes + ((size_t)list * a.code_tiles + (c0 >> 5) + htile) * CODE_TILE_BYTES);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rec[(2 * j + (lane >> 5)) * 32 + (lane & 31)] = hw[j];
+    if (lane < 32) ((float*)(rec + 256))[lane] = hm;
+  };
   for (int tile = wave; tile < ntiles; tile += NW) {
     wave_sync();
     store();
     wave_sync();
+    if constexpr (CODES) {
+      if (htile >= 0) put_codes();
+    }
     if (tile + NW < ntiles) load(tile + NW);
     f32x16 s = {};                                               // S^T = K Q^T, Q operand from LDS
     {
@@ -224,14 +242,35 @@ __global__ __launch_bounds__(64 * NW) void attn_wave_kernel(AttnArgs a) {
       for (int mt4 = 0; mt4 < 4; ++mt4) acc[mt4] *= alpha;
       m = mn;
     }
-    float p[16];
+    float p[16], xr[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      p[r] = exp2_fast(FP8 ? s[r] - m : fmaf(s[r], sl2, -m));
+      xr[r] = FP8 ? s[r] - m : fmaf(s[r], sl2, -m);              // logit - reference, log2 units (<= 8)
+      p[r] = exp2_fast(xr[r]);
       lsum += p[r];
       if (FP8) p[r] *= wvs[crow(lane, r)];
     }
+    if constexpr (CODES) {
+      // Score filter: one byte per (token, row), floor(8 x + 191) clamped to [0, 255] (masked
+      // positions: x = -inf, code 0), four consecutive tokens per word; the tile's record holds
+      // quads 2 j + (lane >> 5) of row lane & 31, then the rows' references.
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t w = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float y = __builtin_amdgcn_fmed3f(fmaf(xr[4 * j + i], 8.f, (float)CODE_OFFSET), 0.f, 255.f);
+          w |= (uint32_t)y << (8 * i);
+        }
+        hw[j] = w;
+      }
+      hm = m;
+      htile = tile;
+    }
     M::template pv<SPLIT>(acc, vt, p, lane);
+  }
+  if constexpr (CODES) {
+    if (htile >= 0) put_codes();
   }
   lsum += __shfl_xor(lsum, 32);
 
@@ -398,50 +437,10 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
     load(kB, sB, nq > 1 ? tstart(1) : cend);
   }
   if (a.part_ml) {
-    // The full layer's merge, folded in (at most 64 chunks): every workgroup derives the LSE of all rows
-    // from the chunk partials; row r's output is merged by workgroup r % nwg of the list's nwg >= 1.
-    const int nchd = (Lb + a.dchunk - 1) / a.dchunk;             // <= 64: one chunk per lane
     const int nwg = CAND ? nper : max(1, (ncand + a.chunk - 1) / a.chunk);
     if (cidx >= nwg) return;
-    const size_t first = (size_t)list * a.dmax_chunks * a.R;
-    // Rows wave + NW i (i < RPW) for the LSE table, and the rows this wave merges: the workgroup's rows
-    // (r % nwg == cidx) taken in turn by its waves, mr_j = cidx + nwg (wave + NW j) < R.  Their chunk
-    // partials are loaded in one batch (lane = chunk), then reduced row by row.
-    constexpr int RPW = (32 + NW - 1) / NW;                      // rows per wave (R <= 32)
-    auto mrow = [&](int j) { return cidx + nwg * (wave + NW * j); };
-    float2 v[2 * RPW];
-#pragma unroll
-    for (int i = 0; i < 2 * RPW; ++i) {
-      const int r = min(i < RPW ? wave + NW * i : mrow(i - RPW), a.R - 1);
-      v[i] = *(const float2*)(a.part_ml + ((first + r) + (size_t)min(lane, nchd - 1) * a.R) * 2);
-      if (lane >= nchd) v[i] = make_float2(-INFINITY, 0.f);
-    }
-    float l2m[RPW];
-#pragma unroll
-    for (int i = 0; i < 2 * RPW; ++i) {
-      const int r = i < RPW ? wave + NW * i : mrow(i - RPW);
-      if (r >= a.R) continue;                                    // uniform over the wave
-      const float mx = wave_max(v[i].x);
-      const float ls = mx == -INFINITY ? 0.f : wave_sum(exp2f(v[i].x - mx) * v[i].y);
-      const float l2 = ls > 0.f ? mx + __log2f(ls) : -INFINITY;
-      if (i < RPW) {
-        if (lane == 0) s_lse2[r] = l2;
-      } else {
-        l2m[i - RPW] = l2;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < RPW; ++j) {
-      const int mr = mrow(j);
-      if (mr >= a.R) break;
-      const float* ml = a.part_ml + (first + mr) * 2;
-      const float2 o = l2m[j] == -INFINITY ? make_float2(0.f, 0.f)
-                                           : merged_o(ml, (size_t)a.R * 2, a.part_acc + (first + mr) * D,
-                                                      (size_t)a.R * D, 0, nchd, 1, l2m[j], lane);
-      const size_t orow = ((size_t)b * a.n_q + mr / a.G) * a.H + (size_t)g * a.G + mr % a.G;
-      *(float2*)(a.out + orow * D + 2 * lane) = o;
-      if (lane == 0 && a.lse) a.lse[orow] = l2m[j] * LN2;
-    }
+    fold_merge<NW>(a.part_acc, a.part_ml, a.dchunk, a.dmax_chunks, a.R, a.G, a.H, a.n_q, b, g, list, Lb, cidx, nwg,
+                   s_lse2, a.out, a.lse, nullptr, wave, lane);
   }
   if (!CAND && c0 >= ncand) return;
   const bool do_hist = a.hist != nullptr;
@@ -530,26 +529,9 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
                                                     s, 0, 0, 0);
       }
       const float f = a.scale_log2 * (FP8 ? ksc[wave][32 * half + (lane & 31)] : 1.f);
-      float p[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) p[r] = exp2_fast(s[r] * f - lse2[r]);
       const int pos = ts + 32 * half + (lane & 31);
       float tv[NQ];
-      if (tpw == 1) {
-        float v = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) v += p[r];
-        tv[0] = v + __shfl_xor(v, 32);
-      } else {
-        float blk[4];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          blk[q4] = p[4 * q4] + p[4 * q4 + 1] + p[4 * q4 + 2] + p[4 * q4 + 3];
-          blk[q4] += __shfl_xor(blk[q4], 32);
-        }
-#pragma unroll
-        for (int t = 0; t < NQ; ++t) tv[t] = tpw == 4 ? blk[t] : blk[2 * t] + blk[2 * t + 1];
-      }
+      tile_scores<NQ>(s, f, lse2, tpw, tv);
       if (lane < 32 && pos < cend) {
 #pragma unroll
         for (int t = 0; t < NQ; ++t) {
@@ -652,7 +634,10 @@ __global__ __launch_bounds__(64 * NW) void scores_wave_kernel(ScoreArgs a) {
 template <int KVT>
 static hipError_t launch_wave_t(const AttnArgs& a, hipStream_t st) {
   constexpr int NW = 8;
-  hipLaunchKernelGGL((attn_wave_kernel<KVT, NW>), dim3(a.n_items), dim3(64 * NW), 0, st, a);
+  if (a.codes)
+    hipLaunchKernelGGL((attn_wave_kernel<KVT, NW, true>), dim3(a.n_items), dim3(64 * NW), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_wave_kernel<KVT, NW, false>), dim3(a.n_items), dim3(64 * NW), 0, st, a);
   return hipGetLastError();
 }
 

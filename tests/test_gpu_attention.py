@@ -96,6 +96,21 @@ def _check_seq(up, res, i, top_k=1024, window=128, check_sparse=True, stats=None
     return hit, tot
 
 
+def _same_lists_without_scores(up, res, top_k=1024, window=128):
+    """The benchmark's form of the full layer (no dense scores asked for: the score filter for one
+    query token) selects exactly the lists the dense scores gave, and its outputs are identical."""
+    from long_context_split_amd import hysparse as hs
+    B, n_q, H, _ = up.q_full.shape
+    out, lse, idx, cnt = hs.full_attn_select(
+        up.kv, up.q_full, top_k, window,
+        sel_idx=torch.full((B, n_q, up.kv.n_kv, top_k + window), -0x7F7F7F7F, dtype=torch.int32, device="cuda"),
+        sel_count=torch.full((B, n_q, up.kv.n_kv), -0x7F7F7F7F, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), res["idx"]), "lists without dense scores"
+    assert np.array_equal(cnt.cpu().numpy(), res["cnt"])
+    assert np.array_equal(out.cpu().numpy(), res["out"]) and np.array_equal(lse.cpu().numpy(), res["lse"])
+
+
 def _recall_report(stats):
     """Plain recall, tie-aware recall and the worst single list (gate G2 uses the plain one)."""
     return (f"recall {stats['hit'] / stats['tot']:.6f} tie-aware {stats['tie'] / stats['tot']:.6f} "
@@ -274,6 +289,7 @@ def test_config2_full_size_sampled():
     banner("config 2 full size: B=32 L=131072 H=32 bf16")
     up = Uploaded(synth.decode_case(2))
     res = _run_block(up)
+    _same_lists_without_scores(up, res)
     stats = {}
     for i in (0, 17, 31):
         banner(f"config 2 oracle on sequence {i}")
@@ -309,6 +325,7 @@ def test_config5_full_size_sampled():
         banner(f"config 5 full size: block {blk}")
         up = Uploaded(synth.decode_case(5, block=blk))
         res = _run_block(up)
+        _same_lists_without_scores(up, res)
         lens = up.case["lengths"]
         for i in (int(np.argmin(lens)), int(np.argmax(lens))):
             banner(f"config 5 block {blk}: oracle on sequence {i} (L={int(lens[i])})")

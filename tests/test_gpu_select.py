@@ -150,10 +150,11 @@ def test_select_blocks_budgets_and_long_list():
                                               (1, 32, 60000, 8, True), (1, 32, 3000, 4, True),
                                               (1, 32, 20000, 33, True)])
 def test_candidate_selection_paths_agree(n_q, H, L, B, ragged, monkeypatch):
-    """The full layer's selection three ways: from the candidates the score pass appends (the
-    default for one query token and at least 16 lists, lowered to 4 here so the few-list cases take
-    it too; no dense scores stored), the same with the dense scores requested, and the dense
-    three-kernel radix select.  All give identical lists,
+    """The full layer's selection four ways: the score filter (the default for one query token
+    without dense scores: bounds from the dense pass's codes, exact scores only for the tokens
+    that can reach the k'-th), the candidates the score pass appends (candidate mode, for one query
+    token and at least 16 lists, lowered to 4 here so the few-list cases take it too), the same with
+    the dense scores requested, and the dense three-kernel radix select.  All give identical lists,
     and the one with scores equals the oracle's selection on those scores.
     L = 1153 leaves most score workgroups without work, L = 300 selects every candidate, 272 lists
     get one score workgroup each (almost every unit is taken from the list's counter), L = 129
@@ -181,12 +182,15 @@ def test_candidate_selection_paths_agree(n_q, H, L, B, ragged, monkeypatch):
     S = hs.scores_stride(kv, 128)
     sc = torch.empty((B, n_q, 1, max(S, 1)), dtype=torch.float32, device="cuda")
     _, _, idx_b, cnt_b = hs.full_attn_select(kv, qd, scores_out=sc)
+    monkeypatch.setenv("HS_SCORE_FILTER", "0")
+    _, _, idx_d, cnt_d = hs.full_attn_select(kv, qd)
     monkeypatch.setenv("HS_DENSE_SELECT", "1")
     _, _, idx_c, cnt_c = hs.full_attn_select(kv, qd)
     torch.cuda.synchronize()
-    ia, ib, ic = idx_a.cpu().numpy(), idx_b.cpu().numpy(), idx_c.cpu().numpy()
-    assert np.array_equal(ia, ib) and np.array_equal(ia, ic)
+    ia, ib, ic, idd = idx_a.cpu().numpy(), idx_b.cpu().numpy(), idx_c.cpu().numpy(), idx_d.cpu().numpy()
+    assert np.array_equal(ia, ib) and np.array_equal(ia, ic) and np.array_equal(ia, idd)
     assert np.array_equal(cnt_a.cpu().numpy(), cnt_c.cpu().numpy())
+    assert np.array_equal(cnt_d.cpu().numpy(), cnt_c.cpu().numpy())
     scores = sc.cpu().numpy()
     for i in range(B):
         Li = lens[i]
