@@ -71,6 +71,12 @@ def parse():
     ap.add_argument("--bridge-iters", type=int, default=10)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device-to-device copy (known bytes, for scaling HBM counters)")
+    ap.add_argument("--no-probe", action="store_true", help="skip the streaming read probe (measured peak)")
+    ap.add_argument("--probe-sizes", action="store_true",
+                    help="also probe repeated reads of 16 MB .. 2 GiB buffers (the Infinity Cache's range)")
+    ap.add_argument("--no-append-step", action="store_true",
+                    help="skip the decode step timed with the KV append through the bridge ahead of it")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the chunked prefill measurement")
     return ap.parse_args()
 
 
@@ -247,8 +253,19 @@ def main():
                      "algorithmic_flops_per_launch": k1_flops, "avg_launch_us": round(k1["avg_ms"] * 1e3, 2),
                      "dominant_kernel_by_time": dom})
 
+    # ---------------------------------------------------------------- measured streaming peak
+    probe = None if args.no_probe else bench_probe(dev, args.probe_sizes)
+    if probe and roof and roof["unit"] == "GB/s":
+        roof["frac_of_measured_peak"] = round(roof["achieved"] / probe["peak_GBps"], 4)
+
+    # ---------------------------------------------------------------- decode step with the KV append
+    append_step = None
+    if not args.no_append_step and spec["kv"] == "bf16" and n_q == 1 and n_blocks == 1 and not args.select_block:
+        append_step = bench_append_step(dev, blocks[0], step, flush, graph is not None, args.steps, H, n_q)
+
     # ---------------------------------------------------------------- KV Bridging (prefill side)
     bridge = None if args.no_bridge else bench_bridge(dev, args.bridge_iters)
+    prefill = None if args.no_prefill else bench_prefill(dev, args.bridge_iters)
     swa = None if args.no_swa else bench_swa(dev, args.bridge_iters, args.swa_window)
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -286,20 +303,191 @@ def main():
         },
         "achieved_hbm_GBps": round(eff_gbps, 1),
         "hbm_frac": round(eff_gbps / HBM_PEAK_GBPS, 4),
+        "hbm_frac_of_measured_peak": round(eff_gbps / probe["peak_GBps"], 4) if probe else None,
         "algorithmic_bytes_per_step": alg_bytes,
         "ms_p10": round(p10, 5), "ms_p90": round(p90, 5),
         "kernels": {n: {"launches_per_step": d["launches"] / args.steps, "avg_us": round(d["avg_ms"] * 1e3, 2)}
                     for n, d in kern.items()},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "stream_probe": probe,
+        "decode_step_with_append": append_step,
         "bridge": bridge,
         "swa": swa,
+        "prefill": prefill,
         "timing": ("HIP-graph replay of the step" if graph is not None else "eager launches") +
                   "; HIP events per step" + ("" if args.flush == "none" else
                                              f"; Infinity Cache flushed between steps by a 1 GiB {args.flush}") +
                   "; kernel durations from per-launch HIP events on the library stream in a second (eager) region",
     }
     print(json.dumps(line), flush=True)
+
+
+def bench_probe(dev, sizes=False):
+    """The practical read ceiling: a 2 GiB buffer read with 16-byte non-temporal loads (the load the
+    dense pass uses) at 256, 512 and 1024 workgroups of 512 threads, best of each over 10 reads with
+    the Infinity Cache evicted in between (the buffer is 8x its size); with sizes, also repeated
+    back-to-back reads of 16 MB .. 2 GiB buffers (below 256 MB they can be served by the cache)."""
+    import torch
+    from long_context_split_amd import hysparse as hs
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    res = {}
+    for nt in (True, False):
+        for grid in (256, 512, 1024):
+            hs.read_probe(buf, nbytes, nt, grid, sink)
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+            for a, b in evs:
+                a.record()
+                hs.read_probe(buf, nbytes, nt, grid, sink)
+                b.record()
+            torch.cuda.synchronize()
+            best = min(a.elapsed_time(b) for a, b in evs)
+            res[f"{'nt' if nt else 'plain'}_grid{grid}"] = round(nbytes / (best * 1e-3) / 1e9, 1)
+    peak = max(v for k, v in res.items() if k.startswith("nt_"))
+    out = {"what": "2 GiB streaming read, 16-byte loads, best of 10 per launch shape", "GBps": res,
+           "peak_GBps": peak, "frac_of_published": round(peak / HBM_PEAK_GBPS, 4)}
+    log(f"stream probe: {peak:.0f} GB/s ({peak / HBM_PEAK_GBPS:.3f} of 8 TB/s); {res}")
+    if sizes:
+        sweep = {}
+        for mb in (16, 64, 128, 192, 256, 512, 2048):
+            nb = mb << 20
+            for _ in range(3):
+                hs.read_probe(buf, nb, True, 256, sink)
+            reps = 50 if mb < 512 else 10
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                hs.read_probe(buf, nb, True, 256, sink)
+            b.record()
+            torch.cuda.synchronize()
+            sweep[f"{mb}MB"] = round(nb * reps / (a.elapsed_time(b) * 1e-3) / 1e9, 1)
+        out["repeated_reads_GBps"] = sweep
+        log(f"repeated reads by buffer size: {sweep}")
+    del buf
+    return out
+
+
+def bench_append_step(dev, bl, step, flush, use_graph, steps, H, n_q):
+    """The decode step with its KV append ahead of it: each sequence's newest token (the last of its
+    L_b rows) is projected from a Self-Decoder hidden state [B, 4096] into four target caches (the
+    block's own bf16 cache and three others) by hs_kv_append, then the full layer and the sparse
+    layers run on the grown cache; timed like the main step."""
+    import ctypes
+    import numpy as np
+    import torch
+    import synth
+    from long_context_split_amd import hysparse as hs
+    kv = bl["kv"]
+    B = kv.batch
+    D, nt = 4096, 4
+    case = synth.bridge_case(4, T=B, D=D, n_targets=nt)
+    x = torch.from_numpy(case["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    wk = [torch.from_numpy(w.view(np.int16)).to(dev).view(torch.bfloat16) for w in case["w_k"]]
+    wv = [torch.from_numpy(w.view(np.int16)).to(dev).view(torch.bfloat16) for w in case["w_v"]]
+    others = [hs.KVCache(torch.empty_like(kv.k), torch.empty_like(kv.v)) for _ in range(nt - 1)]
+    targets = [hs.KVCache(kv.k, kv.v)] + others
+    h_rows = np.ascontiguousarray(kv.h_start + kv.h_seq.astype(np.int64) - 1)
+    d_rows = torch.from_numpy(h_rows).to(dev)
+    aws = hs.workspace(hs.kv_append_workspace_size(B, D, nt), dev)
+    wkp = (ctypes.c_void_p * nt)(*[w.data_ptr() for w in wk])
+    wvp = (ctypes.c_void_p * nt)(*[w.data_ptr() for w in wv])
+    tgp = (ctypes.POINTER(hs.hs_kv_cache) * nt)(*[ctypes.pointer(t._c) for t in targets])
+    hrp = h_rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+    def full_step():
+        hs.check(hs.lib.hs_kv_append(x.data_ptr(), B, D, nt, wkp, wvp, tgp, d_rows.data_ptr(), hrp, aws.data_ptr(),
+                                     aws.numel(), torch.cuda.current_stream().cuda_stream))
+        step()
+
+    for _ in range(3):
+        full_step()
+    torch.cuda.synchronize()
+    graph = None
+    if use_graph:
+        side = torch.cuda.Stream()
+        with torch.cuda.stream(side):
+            full_step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            full_step()
+        graph.replay()
+        torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        flush(i)
+        evs[i][0].record()
+        if graph is not None:
+            graph.replay()
+        else:
+            full_step()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = statistics.median(a.elapsed_time(b) for a, b in evs)
+    hs.timing_enable(True)
+    hs.timing_collect()
+    for i in range(steps):
+        flush(i)
+        full_step()
+    torch.cuda.synchronize()
+    recs = hs.timing_collect()
+    hs.timing_enable(False)
+    app = [t for n, t in recs if n == "kv_append"]
+    app_us = 1e3 * sum(app) / max(1, len(app))
+    log(f"decode step with the KV append ahead: {ms * 1e3:.1f} us ({B * n_q / (ms * 1e-3):.0f} queries/s); "
+        f"append {app_us:.1f} us")
+    return {"workload": f"{B} new tokens x {D} -> {nt} targets (K,V) bf16 at each sequence's newest row, then "
+                        "the full layer + sparse layers on the grown cache",
+            "ms_per_step": round(ms, 5), "queries_per_s": round(B * n_q / (ms * 1e-3), 2),
+            "append_us": round(app_us, 2),
+            "append_bytes": nt * 2 * D * 128 * 2 + B * D * 2 + nt * 2 * B * 128 * 2}
+
+
+def bench_prefill(dev, iters):
+    """A 32768-token prompt prefilled in 4 chunks of 8192 (hs_prefill_chunk): per chunk, sliding-window
+    attention (H = 32 on one bf16 KV head, window 128) over the growing Self-Decoder cache, then KV
+    Bridging of its hidden states [8192, 4096] into 4 FP8 targets at rows 262144 + 8192 c."""
+    import torch
+    from long_context_split_amd import hysparse as hs
+    T, nch, H, w, D, nt, cap, off = 8192, 4, 32, 128, 4096, 4, 1 << 20, 262144
+    P = T * nch
+    g = torch.Generator(device=dev)
+    g.manual_seed(4321)
+    k = torch.randn((P, 1, 128), generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn((P, 1, 128), generator=g, device=dev).to(torch.bfloat16)
+    q = torch.randn((nch, T, H, 128), generator=g, device=dev).to(torch.bfloat16)
+    x = torch.randn((P, D), generator=g, device=dev).to(torch.bfloat16)
+    sd = (2.0 / (D + 128)) ** 0.5
+    wk = [(torch.randn((D, 128), generator=g, device=dev) * sd).to(torch.bfloat16) for _ in range(nt)]
+    wv = [(torch.randn((D, 128), generator=g, device=dev) * sd).to(torch.bfloat16) for _ in range(nt)]
+    tg = [hs.KVCache(torch.empty((cap, 1, 128), dtype=torch.uint8, device=dev),
+                     torch.empty((cap, 1, 128), dtype=torch.uint8, device=dev), None, None,
+                     torch.empty((cap, 1), dtype=torch.float32, device=dev),
+                     torch.empty((cap, 1), dtype=torch.float32, device=dev)) for _ in range(nt)]
+    caches = [hs.KVCache(k, v, [T * (c + 1)], [0]) for c in range(nch)]
+    outs = [torch.empty((1, T, H, 128), dtype=torch.float32, device=dev) for _ in range(nch)]
+
+    def prompt():
+        for c in range(nch):
+            hs.prefill_chunk(caches[c], q[c:c + 1], w, x[c * T:(c + 1) * T], wk, wv, tg, off + c * T, swa_out=outs[c])
+
+    prompt()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in evs:
+        a.record()
+        prompt()
+        b.record()
+    torch.cuda.synchronize()
+    ms = statistics.median(a.elapsed_time(b) for a, b in evs)
+    flops = 2.0 * P * D * nt * 2 * 128 + 4.0 * sum(min(t + 1, w) for t in range(P)) * H * 128
+    log(f"prefill {nch} x {T} tokens: {ms * 1e3:.1f} us ({P / (ms * 1e-3):.0f} tokens/s)")
+    return {"workload": f"{P}-token prompt in {nch} chunks of {T}: sliding-window attention (H={H}, w={w}, bf16) "
+                        f"+ KV Bridging [{T}, {D}] -> {nt} FP8 targets per chunk",
+            "ms": round(ms, 4), "tokens_per_s": round(P / (ms * 1e-3), 1), "flops": flops,
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
 
 
 def fp8_cache(case, dev):

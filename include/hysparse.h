@@ -270,6 +270,27 @@ hs_status hs_sparse_attn_noalloc(const hs_kv_cache *kv, const hs_attn_params *p,
 hs_status hs_swa_attn(const hs_kv_cache *kv, const hs_attn_params *p, const void *q,
                       hs_dtype q_dtype, float *out, void *stream);
 
+/* One prefill chunk of a prompt on the Self-Decoder side, feeding the
+ * Cross-Decoder (ithome page, prefill early-exit paragraphs: prefill runs only
+ * the first half of the layers plus the bridging projections, which fill every
+ * Cross-Decoder full layer's cache; toolnavs page "Prefill は半分で終わる").
+ * Exactly hs_swa_attn(self_kv, swa_p, q, q_dtype, swa_out, stream) followed by
+ * hs_kv_bridge(hidden, n_tokens, d_model, n_targets, w_k, w_v, targets,
+ * row_offset, stream) on the same stream: the chunk's n_tokens queries attend
+ * to their bands of the Self-Decoder cache (the chunk's rows appended at its
+ * end before the call, so bands reach back into earlier chunks), and the
+ * chunk's hidden states are projected into every target at rows
+ * [row_offset, row_offset + n_tokens).  A prompt is prefilled by calling it on
+ * consecutive chunks with growing self_kv lengths and row_offset advancing by
+ * each chunk's size.  self_kv holds one sequence (batch 1) and
+ * swa_p->q_tokens must equal n_tokens.  Every check of both steps runs before
+ * either is launched; errors as the two calls. */
+hs_status hs_prefill_chunk(const hs_kv_cache *self_kv, const hs_attn_params *swa_p, const void *q,
+                           hs_dtype q_dtype, float *swa_out, const void *hidden, int64_t n_tokens,
+                           int32_t d_model, int32_t n_targets, const void *const *w_k,
+                           const void *const *w_v, const hs_kv_cache *const *targets,
+                           int64_t row_offset, void *stream);
+
 /* The selection stage alone, on caller-given float32 scores (a test hook for
  * checking the selection bit for bit).  scores: device float
  * [batch, q_tokens, n_kv, max_len - min(window, max_len)] laid out as
@@ -298,6 +319,16 @@ typedef struct {
 } hs_kernel_time;
 void hs_timing_enable(int enable);
 int hs_timing_collect(hs_kernel_time *out, int max);
+
+/* Streaming read probe, a measurement aid: reads `bytes` (a multiple of 16) of
+ * device memory at buf with 16-byte loads (non-temporal when non_temporal != 0,
+ * the load the decode passes stream their cache with), grid workgroups of 512
+ * threads, four loads in flight per thread.  Timed around the call it gives
+ * the practical read ceiling (HBM for buffers larger than the 256 MB Infinity
+ * Cache, the cache for repeated reads of smaller ones).  sink: 16 device bytes
+ * that are never written for real data.  Errors: HS_ERR_INVALID_ARGUMENT. */
+hs_status hs_read_probe(const void *buf, size_t bytes, int non_temporal, int32_t grid, void *sink,
+                        void *stream);
 
 const char *hs_status_string(hs_status s);
 /* Text of the calling thread's last error ("" if none). */

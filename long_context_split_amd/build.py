@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libhysparse.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["hs_attn.hip", "hs_wave.hip", "hs_rows.hip", "hs_gather.hip", "hs_select.hip", "hs_bridge.hip", "hs_append.hip", "hs_swa.hip", "hs_filter.hip", "hs_api.hip"]
+SOURCES = ["hs_attn.hip", "hs_wave.hip", "hs_rows.hip", "hs_gather.hip", "hs_select.hip", "hs_bridge.hip", "hs_append.hip", "hs_swa.hip", "hs_filter.hip", "hs_probe.hip", "hs_api.hip"]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 ALU ops are kept out of the generated code

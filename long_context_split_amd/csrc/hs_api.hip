@@ -433,6 +433,55 @@ hs_status sparse_attn_impl(const hs_kv_cache* kv, const hs_attn_params* p, const
                            const int32_t* sel_idx, const int32_t* sel_count, float* out, void* workspace,
                            size_t workspace_bytes, bool noalloc, void* stream);
 
+// hs_swa_attn's checks and launch arguments (nothing is launched here).
+hs_status swa_prepare(const hs_kv_cache* kv, const hs_attn_params* p, const void* q, hs_dtype q_dtype, float* out,
+                      hs::AttnArgs& a) {
+  CacheInfo ci;
+  hs_status st = check_cache(kv, ci, true);
+  if (st != HS_OK) return st;
+  if (!p) return fail(HS_ERR_INVALID_ARGUMENT, "params is NULL");
+  if (p->num_q_heads < 1 || p->num_q_heads % ci.n_kv)
+    return fail(HS_ERR_INVALID_ARGUMENT, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
+                p->num_q_heads, ci.n_kv);
+  if (p->window < 1) return fail(HS_ERR_INVALID_ARGUMENT, "window %d must be >= 1", p->window);
+  if (!(p->softmax_scale >= 0.f) || !isfinite(p->softmax_scale))
+    return fail(HS_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
+  if (p->q_tokens < 1) return fail(HS_ERR_INVALID_ARGUMENT, "q_tokens %d", p->q_tokens);
+  for (int b = 0; b < kv->batch; ++b)
+    if (p->q_tokens > kv->h_seq_len[b])
+      return fail(HS_ERR_INVALID_ARGUMENT, "q_tokens %d > seq_len[%d] = %d", p->q_tokens, b, kv->h_seq_len[b]);
+  if (!q || !out) return fail(HS_ERR_INVALID_ARGUMENT, "q/out is NULL");
+  if (q_dtype != HS_BF16) return fail(HS_ERR_UNSUPPORTED, "q dtype must be BF16");
+  if (kv->dtype == HS_F32) return fail(HS_ERR_UNSUPPORTED, "F32 caches are not supported here");
+  if (!aligned16(q) || !aligned16(out)) return fail(HS_ERR_INVALID_ARGUMENT, "q/out not 16-byte aligned");
+  if ((int64_t)kv->batch * ci.n_kv > MAX_LISTS) return fail(HS_ERR_UNSUPPORTED, "batch * num_kv_heads > 65535");
+  a = hs::AttnArgs{};
+  a.k = kv->k; a.v = kv->v; a.k_scale = kv->k_scale; a.v_scale = kv->v_scale;
+  a.row_start = kv->d_row_start; a.seq_len = kv->d_seq_len;
+  a.q = q; a.q_f32 = 0;
+  a.n_kv = ci.n_kv; a.H = p->num_q_heads; a.G = p->num_q_heads / ci.n_kv; a.n_q = p->q_tokens;
+  a.R = a.G; a.n_lists = kv->batch * ci.n_kv;
+  a.scale_log2 = scale_log2(p);
+  a.out = out; a.window = p->window;
+  return HS_OK;
+}
+
+// hs_kv_bridge's checks and launch arguments (nothing is launched here).
+hs_status bridge_prepare(const void* hidden, int64_t n_tokens, int32_t d_model, int32_t n_targets,
+                         const void* const* w_k, const void* const* w_v, const hs_kv_cache* const* targets,
+                         int64_t row_offset, hs::BridgeArgs& a) {
+  a = hs::BridgeArgs{};
+  hs_status st = bridge_args(hidden, n_tokens, d_model, n_targets, w_k, w_v, targets, a);
+  if (st != HS_OK) return st;
+  if (row_offset < 0) return fail(HS_ERR_INVALID_ARGUMENT, "row_offset %lld", (long long)row_offset);
+  for (int l = 0; l < n_targets; ++l)
+    if (row_offset + n_tokens > targets[l]->capacity_rows)
+      return fail(HS_ERR_INVALID_ARGUMENT, "target %d: rows [%lld, %lld) exceed capacity %lld", l,
+                  (long long)row_offset, (long long)(row_offset + n_tokens), (long long)targets[l]->capacity_rows);
+  a.row_offset = row_offset;
+  return HS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -466,6 +515,18 @@ int hs_timing_collect(hs_kernel_time* out, int max) {
   }
   g_recs.clear();
   return ok ? n : -1;
+}
+
+hs_status hs_read_probe(const void* buf, size_t bytes, int non_temporal, int32_t grid, void* sink, void* stream) {
+  g_last_error.clear();
+  if (!buf || !sink) return fail(HS_ERR_INVALID_ARGUMENT, "buf/sink is NULL");
+  if (!aligned16(buf) || !aligned16(sink) || bytes % 16)
+    return fail(HS_ERR_INVALID_ARGUMENT, "buf/sink not 16-byte aligned or bytes %zu not a multiple of 16", bytes);
+  if (grid < 1 || grid > 65535) return fail(HS_ERR_INVALID_ARGUMENT, "grid %d", grid);
+  hipError_t e = timed("read_probe", (hipStream_t)stream,
+                       [&] { return hs::launch_read_probe(buf, bytes, non_temporal, grid, sink, (hipStream_t)stream); });
+  if (e != hipSuccess) return hip_fail(e, "read probe");
+  return HS_OK;
 }
 
 size_t hs_full_attn_select_workspace_size(const hs_kv_cache* kv, const hs_attn_params* p) {
@@ -701,33 +762,9 @@ hs_status hs_sparse_attn_noalloc(const hs_kv_cache* kv, const hs_attn_params* p,
 hs_status hs_swa_attn(const hs_kv_cache* kv, const hs_attn_params* p, const void* q, hs_dtype q_dtype,
                       float* out, void* stream) {
   g_last_error.clear();
-  CacheInfo ci;
-  hs_status st = check_cache(kv, ci, true);
-  if (st != HS_OK) return st;
-  if (!p) return fail(HS_ERR_INVALID_ARGUMENT, "params is NULL");
-  if (p->num_q_heads < 1 || p->num_q_heads % ci.n_kv)
-    return fail(HS_ERR_INVALID_ARGUMENT, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
-                p->num_q_heads, ci.n_kv);
-  if (p->window < 1) return fail(HS_ERR_INVALID_ARGUMENT, "window %d must be >= 1", p->window);
-  if (!(p->softmax_scale >= 0.f) || !isfinite(p->softmax_scale))
-    return fail(HS_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
-  if (p->q_tokens < 1) return fail(HS_ERR_INVALID_ARGUMENT, "q_tokens %d", p->q_tokens);
-  for (int b = 0; b < kv->batch; ++b)
-    if (p->q_tokens > kv->h_seq_len[b])
-      return fail(HS_ERR_INVALID_ARGUMENT, "q_tokens %d > seq_len[%d] = %d", p->q_tokens, b, kv->h_seq_len[b]);
-  if (!q || !out) return fail(HS_ERR_INVALID_ARGUMENT, "q/out is NULL");
-  if (q_dtype != HS_BF16) return fail(HS_ERR_UNSUPPORTED, "q dtype must be BF16");
-  if (kv->dtype == HS_F32) return fail(HS_ERR_UNSUPPORTED, "F32 caches are not supported here");
-  if (!aligned16(q) || !aligned16(out)) return fail(HS_ERR_INVALID_ARGUMENT, "q/out not 16-byte aligned");
-  if ((int64_t)kv->batch * ci.n_kv > MAX_LISTS) return fail(HS_ERR_UNSUPPORTED, "batch * num_kv_heads > 65535");
   hs::AttnArgs a{};
-  a.k = kv->k; a.v = kv->v; a.k_scale = kv->k_scale; a.v_scale = kv->v_scale;
-  a.row_start = kv->d_row_start; a.seq_len = kv->d_seq_len;
-  a.q = q; a.q_f32 = 0;
-  a.n_kv = ci.n_kv; a.H = p->num_q_heads; a.G = p->num_q_heads / ci.n_kv; a.n_q = p->q_tokens;
-  a.R = a.G; a.n_lists = kv->batch * ci.n_kv;
-  a.scale_log2 = scale_log2(p);
-  a.out = out; a.window = p->window;
+  hs_status st = swa_prepare(kv, p, q, q_dtype, out, a);
+  if (st != HS_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = timed("swa_attn", s, [&] { return hs::launch_swa_attn(a, kv_type(kv->dtype), s); });
   if (e != hipSuccess) return hip_fail(e, "sliding-window attention");
@@ -784,18 +821,34 @@ hs_status hs_kv_bridge(const void* hidden, int64_t n_tokens, int32_t d_model, in
                        const void* const* w_k, const void* const* w_v, const hs_kv_cache* const* targets,
                        int64_t row_offset, void* stream) {
   g_last_error.clear();
-  hs::BridgeArgs a{};
-  hs_status st = bridge_args(hidden, n_tokens, d_model, n_targets, w_k, w_v, targets, a);
+  hs::BridgeArgs a;
+  hs_status st = bridge_prepare(hidden, n_tokens, d_model, n_targets, w_k, w_v, targets, row_offset, a);
   if (st != HS_OK) return st;
-  if (row_offset < 0) return fail(HS_ERR_INVALID_ARGUMENT, "row_offset %lld", (long long)row_offset);
-  for (int l = 0; l < n_targets; ++l)
-    if (row_offset + n_tokens > targets[l]->capacity_rows)
-      return fail(HS_ERR_INVALID_ARGUMENT, "target %d: rows [%lld, %lld) exceed capacity %lld", l,
-                  (long long)row_offset, (long long)(row_offset + n_tokens), (long long)targets[l]->capacity_rows);
   if (n_tokens == 0) return HS_OK;
-  a.row_offset = row_offset;
   hipError_t e = timed("kv_bridge", (hipStream_t)stream, [&] { return hs::launch_bridge(a, (hipStream_t)stream); });
   if (e != hipSuccess) return hip_fail(e, "kv bridge");
+  return HS_OK;
+}
+
+hs_status hs_prefill_chunk(const hs_kv_cache* self_kv, const hs_attn_params* swa_p, const void* q, hs_dtype q_dtype,
+                           float* swa_out, const void* hidden, int64_t n_tokens, int32_t d_model, int32_t n_targets,
+                           const void* const* w_k, const void* const* w_v, const hs_kv_cache* const* targets,
+                           int64_t row_offset, void* stream) {
+  g_last_error.clear();
+  hs::AttnArgs sa;
+  hs_status st = swa_prepare(self_kv, swa_p, q, q_dtype, swa_out, sa);
+  if (st != HS_OK) return st;
+  if (self_kv->batch != 1) return fail(HS_ERR_INVALID_ARGUMENT, "the chunk belongs to one prompt: batch %d", self_kv->batch);
+  if (swa_p->q_tokens != n_tokens)
+    return fail(HS_ERR_INVALID_ARGUMENT, "q_tokens %d != n_tokens %lld: the chunk's queries and hidden states",
+                swa_p->q_tokens, (long long)n_tokens);
+  hs::BridgeArgs ba;
+  if ((st = bridge_prepare(hidden, n_tokens, d_model, n_targets, w_k, w_v, targets, row_offset, ba)) != HS_OK)
+    return st;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = timed("swa_attn", s, [&] { return hs::launch_swa_attn(sa, kv_type(self_kv->dtype), s); });
+  if (e != hipSuccess) return hip_fail(e, "sliding-window attention");
+  if ((e = timed("kv_bridge", s, [&] { return hs::launch_bridge(ba, s); })) != hipSuccess) return hip_fail(e, "kv bridge");
   return HS_OK;
 }
 

@@ -86,6 +86,9 @@ lib.hs_sparse_attn_noalloc.restype = ctypes.c_int
 lib.hs_sparse_attn_noalloc.argtypes = [_KVP, _PP, _P, ctypes.c_int, _P, _P, _P, _P]
 lib.hs_swa_attn.restype = ctypes.c_int
 lib.hs_swa_attn.argtypes = [_KVP, _PP, _P, ctypes.c_int, _P, _P]
+lib.hs_prefill_chunk.restype = ctypes.c_int
+lib.hs_prefill_chunk.argtypes = [_KVP, _PP, _P, ctypes.c_int, _P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                 ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_KVP), ctypes.c_int64, _P]
 lib.hs_select_from_scores.restype = ctypes.c_int
 lib.hs_select_from_scores.argtypes = [_P, _P, ctypes.POINTER(ctypes.c_int32)] + [ctypes.c_int32] * 7 + \
     [_P, _P, _P, ctypes.c_size_t, _P]
@@ -103,6 +106,8 @@ class hs_kernel_time(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char_p), ("ms", ctypes.c_float)]
 
 
+lib.hs_read_probe.restype = ctypes.c_int
+lib.hs_read_probe.argtypes = [_P, ctypes.c_size_t, ctypes.c_int, ctypes.c_int32, _P, _P]
 lib.hs_timing_enable.restype = None
 lib.hs_timing_enable.argtypes = [ctypes.c_int]
 lib.hs_timing_collect.restype = ctypes.c_int
@@ -314,6 +319,24 @@ def kv_bridge(hidden, w_k, w_v, targets, row_offset, stream=None):
                            _stream(stream)))
 
 
+def prefill_chunk(self_kv, q, window, hidden, w_k, w_v, targets, row_offset, swa_out=None, softmax_scale=0.0,
+                  stream=None):
+    """One Self-Decoder prefill chunk: sliding-window attention of the chunk's queries q [1, T, H, 128]
+    (the chunk's rows are the last T rows of self_kv) and KV Bridging of its hidden states [T, Dm] into
+    every target at rows [row_offset, row_offset + T).  Returns the attention output [1, T, H, 128]."""
+    B, T, H, d = q.shape
+    p = params(H, T, 0, window, softmax_scale)
+    if swa_out is None:
+        swa_out = torch.empty((B, T, H, d), dtype=torch.float32, device=q.device)
+    n = len(targets)
+    wk = (ctypes.c_void_p * n)(*[w.data_ptr() for w in w_k])
+    wv = (ctypes.c_void_p * n)(*[w.data_ptr() for w in w_v])
+    tg = (_KVP * n)(*[ctypes.pointer(t._c) for t in targets])
+    check(lib.hs_prefill_chunk(self_kv.c, ctypes.byref(p), _ptr(q), query_dtype(q), _ptr(swa_out), _ptr(hidden),
+                               hidden.shape[0], hidden.shape[1], n, wk, wv, tg, int(row_offset), _stream(stream)))
+    return swa_out
+
+
 def kv_append_workspace_size(n_tokens, d_model, n_targets):
     return lib.hs_kv_append_workspace_size(n_tokens, d_model, n_targets)
 
@@ -333,6 +356,14 @@ def kv_append(hidden, w_k, w_v, targets, rows, ws=None, stream=None):
                            h_rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _ptr(ws), ws.numel(),
                            _stream(stream)))
     return d_rows
+
+
+def read_probe(buf, nbytes=None, non_temporal=True, grid=256, sink=None, stream=None):
+    """Streaming read of a device tensor's first nbytes (the measured-peak probe)."""
+    nbytes = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
+    if sink is None:
+        sink = torch.empty(4, dtype=torch.int32, device=buf.device)
+    check(lib.hs_read_probe(_ptr(buf), nbytes, 1 if non_temporal else 0, grid, _ptr(sink), _stream(stream)))
 
 
 def timing_enable(on=True):

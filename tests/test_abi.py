@@ -235,3 +235,21 @@ def test_sparse_attn_noalloc_rejects_before_launch(hs):
     pb = hs.params(128, 1)
     assert f(ctypes.byref(big), ctypes.byref(pb), 0x200000, 0, 0x500000, 0x600000, 0x400000, None) == 2
     assert "static" in hs.last_error()
+
+
+def test_prefill_chunk_rejects_before_launch(hs):
+    """The chunk driver checks both of its steps (and that they describe the same chunk) first."""
+    f = hs.lib.hs_prefill_chunk
+    tgt = _cache(hs, dtype=2, scales=True, lens=(1,), cap=1000)
+    tp = (ctypes.POINTER(hs.hs_kv_cache) * 1)(ctypes.pointer(tgt))
+    w = (ctypes.c_void_p * 1)(0x800000)
+    one = _cache(hs, lens=(300,), cap=1000)
+    two = _cache(hs, lens=(300, 200), cap=1000)
+    p = hs.params(32, 100, 0, 128)
+    args = lambda kv, prm, n, off: (ctypes.byref(kv), ctypes.byref(prm), 0x200000, 1, 0x400000, 0x900000, n, 512,
+                                    1, w, w, tp, off, None)
+    assert f(*args(two, p, 100, 0)) == 1                            # two sequences
+    assert f(*args(one, p, 99, 0)) == 1                             # q_tokens != n_tokens
+    assert f(*args(one, p, 100, 950)) == 1                          # bridge rows past the target capacity
+    assert f(*args(one, hs.params(32, 100, 0, 0), 100, 0)) == 1     # window < 1
+    assert f(*args(one, hs.params(32, 400, 0, 128), 400, 0)) == 1   # more queries than cache rows
