@@ -80,5 +80,39 @@ def build(verbose=False, jobs=None, force=False):
     return LIB
 
 
+# Host-code sanitizers for the C ABI layer: hs_api.hip (argument checks, planning, launch
+# sequencing) is compiled with AddressSanitizer and UndefinedBehaviorSanitizer on its host side
+# only (each -fsanitize= after -Xarch_host; the device code is built as usual) and linked with the
+# regular objects of the kernel sources.  Loaded with the clang ASan runtime preloaded.
+SANITIZED_LIB = os.path.join(OBJ, "libhysparse_sanitized.so")
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+
+
+def asan_runtime():
+    """Path of the clang AddressSanitizer runtime of this ROCm toolchain, or None."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return hits[-1] if hits else None
+
+
+def build_sanitized(verbose=False):
+    build(verbose=verbose)                                   # the kernel objects
+    obj = os.path.join(OBJ, "hs_api_sanitized.o")
+    cmd = [HIPCC] + FLAGS + SANITIZE + ["-c", os.path.join(CSRC, "hs_api.hip"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for the sanitized hs_api.hip:\n" + r.stderr)
+    objs = [os.path.join(OBJ, f.replace(".hip", ".o")) for f in SOURCES if f != "hs_api.hip"] + [obj]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", SANITIZED_LIB] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stderr)
+    return SANITIZED_LIB
+
+
 if __name__ == "__main__":
-    build(verbose=True, force="--force" in sys.argv)
+    if "--sanitized" in sys.argv:
+        print(build_sanitized(verbose=True))
+    else:
+        build(verbose=True, force="--force" in sys.argv)

@@ -97,8 +97,12 @@ struct CacheInfo {
 hs_status check_cache(const hs_kv_cache* kv, CacheInfo& ci, bool need_rows) {
   if (!kv) return fail(HS_ERR_INVALID_ARGUMENT, "kv is NULL");
   if (kv->head_dim != 128) return fail(HS_ERR_UNSUPPORTED, "head_dim %d (only 128 is supported)", kv->head_dim);
-  if (kv->dtype != HS_F32 && kv->dtype != HS_BF16 && kv->dtype != HS_FP8_E4M3)
-    return fail(HS_ERR_INVALID_ARGUMENT, "unknown cache dtype %d", (int)kv->dtype);
+  // A C caller may store any int in the enum field; read it as one before it is known to be valid
+  // (a C++ load of an hs_dtype outside its enumerators is undefined).
+  int32_t dt;
+  memcpy(&dt, &kv->dtype, sizeof dt);
+  if (dt != HS_F32 && dt != HS_BF16 && dt != HS_FP8_E4M3)
+    return fail(HS_ERR_INVALID_ARGUMENT, "unknown cache dtype %d", (int)dt);
   if (kv->num_kv_heads < 1) return fail(HS_ERR_INVALID_ARGUMENT, "num_kv_heads %d", kv->num_kv_heads);
   if (!kv->k || !kv->v) return fail(HS_ERR_INVALID_ARGUMENT, "cache k/v pointer is NULL");
   if (!aligned16(kv->k) || !aligned16(kv->v)) return fail(HS_ERR_INVALID_ARGUMENT, "cache k/v not 16-byte aligned");

@@ -12,7 +12,8 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libhysparse.so")
+# HYSPARSE_LIB selects another build of the same library (the host-sanitized one in the tests)
+LIB_PATH = os.environ.get("HYSPARSE_LIB") or os.path.join(_HERE, "libhysparse.so")
 
 HS_OK, HS_ERR_INVALID_ARGUMENT, HS_ERR_UNSUPPORTED, HS_ERR_WORKSPACE_TOO_SMALL, HS_ERR_HIP = range(5)
 HS_F32, HS_BF16, HS_FP8_E4M3 = 0, 1, 2
