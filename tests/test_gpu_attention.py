@@ -212,6 +212,54 @@ def test_sparse_lists_with_absent_entries(kvtype, H, schunk, monkeypatch):
     print(f"[result] absent-entry lists kv={kvtype} H={H} chunk={schunk} max|dO| {worst:.3e}", flush=True)
 
 
+@pytest.mark.parametrize("kvtype,H", [("bf16", 32), ("e4m3", 64)])
+def test_sparse_workspace_contents_do_not_matter(kvtype, H):
+    """The sparse layer's workspace (chunk partials) is scratch: filled with random bytes, then
+    reused by a second call and a third with other counts, every output equals the output of the
+    same call on a zero-filled workspace bit for bit, and the oracle's within the layer's
+    tolerance."""
+    from long_context_split_amd import hysparse as hs
+    banner(f"sparse layer, random-filled and reused workspace kv={kvtype} H={H}")
+    rng = np.random.default_rng(5)
+    lens = [20000, 1300, 5000, 129, 70000, 3000]
+    nb = len(lens)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    tot = sum(lens)
+    kf = rng.standard_normal((tot, 1, 128)).astype(np.float32)
+    vf = rng.standard_normal((tot, 1, 128)).astype(np.float32)
+    q = synth.bf16_bits(rng.standard_normal((nb, 1, H, 128)).astype(np.float32))
+    if kvtype == "bf16":
+        kf, vf = synth.bf16_bits(kf), synth.bf16_bits(vf)
+    case = dict(spec=dict(kv=kvtype, q="bf16"), lengths=np.array(lens), row_start=starts,
+                q_full=q, q_sparse=[q], k=kf, v=vf, needles=[[] for _ in lens])
+    up = Uploaded(case)
+    p = hs.params(H, 1)
+    wsz = hs.sparse_attn_workspace_size(up.kv, p)
+    ws = torch.randint(0, 256, (wsz,), dtype=torch.uint8, device="cuda")
+    for call in range(3):
+        idx = np.full((nb, 1, 1, 1152), -1, np.int32)
+        cnt = np.zeros((nb, 1, 1), np.int32)
+        for i, L in enumerate(lens):
+            n = min(L, 1152 - (200 if call == 2 and i % 2 else 0))
+            idx[i, 0, 0, :n] = rng.choice(L, n, replace=False)
+            cnt[i] = n
+        di, dc = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
+        poison = torch.full((nb, 1, H, 128), float("nan"), dtype=torch.float32, device="cuda")
+        a = hs.sparse_attn(up.kv, up.q_sparse[0], di, dc, ws=ws, out=poison)
+        b = hs.sparse_attn(up.kv, up.q_sparse[0], di, dc, ws=torch.zeros(wsz, dtype=torch.uint8, device="cuda"))
+        torch.cuda.synchronize()
+        a, b = a.cpu().numpy(), b.cpu().numpy()
+        assert np.array_equal(a, b), f"call {call}"
+        worst = 0.0
+        for i in range(nb):
+            qs, k, v = up.oracle_seq(i, "sparse", 0)
+            sel = idx[i, 0, 0, :cnt[i, 0, 0]]
+            ref, _ = attention.sparse_attention(qs, k, v, sel.reshape(1, 1, -1), np.array([[sel.size]]))
+            e = float(np.abs(a[i] - ref).max())
+            worst = max(worst, e)
+            assert e <= TOL[kvtype], f"call {call} seq {i}: max|dO| = {e}"
+        print(f"[result] reused random workspace kv={kvtype} H={H} call {call}: max|dO| {worst:.3e}", flush=True)
+
 def test_gqa_multi_query_tokens_bf16():
     """n_kv = 2 KV heads of 16 query heads each, 3 query tokens (no mask among them)."""
     banner("gqa n_kv=2 H=32 n_q=3 bf16")
