@@ -330,6 +330,16 @@ int hs_timing_collect(hs_kernel_time *out, int max);
 hs_status hs_read_probe(const void *buf, size_t bytes, int non_temporal, int32_t grid, void *sink,
                         void *stream);
 
+/* Self-check of the FP8 storage conversion on the running device (for tests):
+ * hs_kv_bridge (and hs_kv_append above 128 tokens, which runs the same
+ * kernel) rounds to E4M3 with the hardware packed conversion; this compares it
+ * with a bit-level round-to-nearest-even reference (the FP8 rule above
+ * hs_kv_bridge) on every finite float32 y with |y| < 464, the range those
+ * calls use.  counts: device, two 64-bit words,
+ * set to (mismatches, values compared = 2 * 0x43E80000).  Errors:
+ * HS_ERR_INVALID_ARGUMENT (NULL or misaligned counts). */
+hs_status hs_e4m3_check(unsigned long long *counts, void *stream);
+
 const char *hs_status_string(hs_status s);
 /* Text of the calling thread's last error ("" if none). */
 const char *hs_last_error(void);

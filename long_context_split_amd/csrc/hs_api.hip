@@ -533,6 +533,15 @@ hs_status hs_read_probe(const void* buf, size_t bytes, int non_temporal, int32_t
   return HS_OK;
 }
 
+hs_status hs_e4m3_check(unsigned long long* counts, void* stream) {
+  g_last_error.clear();
+  if (!counts) return fail(HS_ERR_INVALID_ARGUMENT, "counts is NULL");
+  if ((uintptr_t)counts % 8) return fail(HS_ERR_INVALID_ARGUMENT, "counts not 8-byte aligned");
+  hipError_t e = timed("e4m3_check", (hipStream_t)stream, [&] { return hs::launch_e4m3_check(counts, (hipStream_t)stream); });
+  if (e != hipSuccess) return hip_fail(e, "e4m3 check");
+  return HS_OK;
+}
+
 size_t hs_full_attn_select_workspace_size(const hs_kv_cache* kv, const hs_attn_params* p) {
   // a size query leaves the caller's last error as it was
   const std::string saved = g_last_error;

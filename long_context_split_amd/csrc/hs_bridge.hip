@@ -19,6 +19,12 @@
 // Tile order: the workgroups of one token tile (all targets) are adjacent in dispatch order and land
 // on one XCD, so they share that tile's X rows through the XCD's L2.
 
+// Epilogue in registers: the row amax by lane shuffles, x / scale correctly rounded, E4M3 by the
+// hardware packed conversion (equal to the software RNE conversion for
+// every finite |y| < 448 that does not round to zero, the range used here; a zero magnitude is stored
+// as +0), then a byte (or bf16) transpose inside each quad of lanes so that every store writes whole
+// cache rows.
+
 #include "hs_common.hpp"
 #include "hs_internal.hpp"
 
@@ -29,8 +35,7 @@ constexpr int BM = 256, BN = 256, BK = 64, NT = 512;
 constexpr int AROW = BK * 2 + 16;               // 144 B per X row in LDS
 constexpr int WROW = 576;                       // bytes per k row of W (256 columns) in LDS
 constexpr int STAGE = BM * AROW + BK * WROW;
-constexpr int EPI = 8 * 64 * 128 * 2;           // per-wave 64 x 128 bf16 staging
-constexpr int SMEM = 2 * STAGE > EPI ? 2 * STAGE : EPI;
+constexpr int SMEM = 2 * STAGE;
 constexpr int APT = BM * BK * 2 / 16 / NT;      // X pieces per thread per stage (4)
 constexpr int BPT = BK * BN * 2 / 16 / NT;      // W pieces per thread per stage (4)
 static_assert(APT == 4 && BPT == 4, "load split");
@@ -147,13 +152,28 @@ __global__ __launch_bounds__(NT) void bridge_kernel(BridgeArgs a) {
     __syncthreads();
   }
 
-  // ---- epilogue: this wave holds rows 64 wm + [0, 64) of head block (tgt, wn)
+  // ---- epilogue: this wave holds rows 64 wm + [0, 64) of head block (tgt, wn), all in registers.
+  // Lane l holds, for rows 32 i + crow(l, r), the columns 32 j + (l & 31), j = 0..3.  Within a quad of
+  // lanes 4 m + t, a byte (or bf16) transpose leaves lane 4 m + t with columns 32 t + 4 m .. + 3 of the
+  // row, so one store per (i, r) writes two whole rows (lanes 0..31 one row, 32..63 the other).
   const int blk = 2 * tgt + wn;
-  char* const ep = smem + wave * (64 * 128 * 2);
-  const int64_t t0 = m0 + 64 * wm;                               // first token of this wave's rows
+  const int64_t t0 = m0 + 64 * wm;                              // first token of this wave's rows
   auto orow = [&](int rl) -> int64_t { return a.rows ? a.rows[t0 + rl] : a.row_offset + t0 + rl; };
+  char* const dst = (char*)a.out[blk];
+  const int qt = lane & 3, qm = (lane & 31) >> 2;
+  // byte selectors of v_perm_b32 {hi, lo}: byte qt of lo -> byte 0, byte qt of hi -> byte 1 (0x0C: zero)
+  const uint32_t sel_lo = (uint32_t)qt | (uint32_t)(4 + qt) << 8 | 0x0C0C0000u;
+  const uint32_t sel_hi = 0x00000C0Cu | (uint32_t)qt << 16 | (uint32_t)(4 + qt) << 24;
+  auto quad = [](uint32_t w, int k) -> uint32_t {               // w of quad lane k (quad_perm [k, k, k, k])
+    switch (k) {
+      case 0: return (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0x00, 0xF, 0xF, false);
+      case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0x55, 0xF, 0xF, false);
+      case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0xAA, 0xF, 0xF, false);
+      default: return (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0xFF, 0xF, 0xF, false);
+    }
+  };
   if (a.fp8) {
-    float* sc = a.scale[blk];
+    float* const sc = a.scale[blk];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -165,41 +185,81 @@ __global__ __launch_bounds__(NT) void bridge_kernel(BridgeArgs a) {
         for (int o = 1; o < 32; o <<= 1) am = fmaxf(am, __shfl_xor(am, o));
         float scale = am / 448.0f;                                   // correctly rounded
         if (scale == 0.f) scale = 1.f;
-        const int rl = 32 * i + crow(lane, r);
+        float y[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          ep[rl * 128 + 32 * j + (lane & 31)] = (char)f32_to_e4m3_rne(acc[i][j][r] / scale);
-        if ((lane & 31) == 0 && t0 + rl < a.T) sc[orow(rl)] = scale;
+        for (int j = 0; j < 4; ++j) y[j] = acc[i][j][r] / scale;     // correctly rounded
+        // bytes j = 0..3 (|y| <= 448 (1 + 2^-24) here)
+        const uint32_t w = e4m3x4_hw(y[0], y[1], y[2], y[3]);
+        const uint32_t q0 = quad(w, 0), q1 = quad(w, 1), q2 = quad(w, 2), q3 = quad(w, 3);
+        const uint32_t out = __builtin_amdgcn_perm(q1, q0, sel_lo) | __builtin_amdgcn_perm(q3, q2, sel_hi);
+        const int rl = 32 * i + crow(lane, r);
+        if (t0 + rl < a.T) {
+          const int64_t orw = orow(rl);
+          *(uint32_t*)(dst + orw * 128 + 32 * qt + 4 * qm) = out;
+          if ((lane & 31) == 0) sc[orw] = scale;
+        }
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    char* dst = (char*)a.out[blk];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int p = lane + 64 * i, rl = p >> 3, c = p & 7;
-      if (t0 + rl < a.T) *(u32x4*)(dst + orow(rl) * 128 + c * 16) = *(const u32x4*)(ep + rl * 128 + c * 16);
-    }
   } else {
-    uint16_t* e16 = (uint16_t*)ep;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
+      for (int r = 0; r < 16; ++r) {
+        // p01 = bf16 of tiles (0, 1), p23 = tiles (2, 3); lane 4 m + t takes tile t of quad lanes 0..3
+        const uint32_t p01 = f32_to_bf16_rne(acc[i][0][r]) | f32_to_bf16_rne(acc[i][1][r]) << 16;
+        const uint32_t p23 = f32_to_bf16_rne(acc[i][2][r]) | f32_to_bf16_rne(acc[i][3][r]) << 16;
+        uint32_t x[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          e16[(32 * i + crow(lane, r)) * 128 + 32 * j + (lane & 31)] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    char* dst = (char*)a.out[blk];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int p = lane + 64 * i, rl = p >> 4, c = p & 15;
-      if (t0 + rl < a.T) *(u32x4*)(dst + orow(rl) * 256 + c * 16) = *(const u32x4*)(ep + rl * 256 + c * 16);
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t a01 = quad(p01, k), a23 = quad(p23, k);
+          x[k] = qt >> 1 ? a23 : a01;
+        }
+        // half (qt & 1) of x[k] -> element k
+        const uint32_t hs = (qt & 1) ? 0x07060302u : 0x05040100u;   // {hi.half, lo.half} byte pairs
+        const uint32_t o0 = __builtin_amdgcn_perm(x[1], x[0], hs);
+        const uint32_t o1 = __builtin_amdgcn_perm(x[3], x[2], hs);
+        const int rl = 32 * i + crow(lane, r);
+        if (t0 + rl < a.T) {
+          uint32_t* d = (uint32_t*)(dst + orow(rl) * 256 + 64 * qt + 8 * qm);
+          *(u32x2*)d = u32x2{o0, o1};
+        }
+      }
     }
   }
+}
+
+// Every float32 bit pattern: the bridge's E4M3 conversion (e4m3x4_hw) against f32_to_e4m3_rne on the
+// finite values with |y| < 464; counts[0] += mismatches, counts[1] += values compared.
+__global__ __launch_bounds__(256) void e4m3_check_kernel(unsigned long long* counts) {
+  unsigned long long bad = 0, n = 0;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x * 4;
+  for (uint64_t u0 = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; u0 < (1ull << 32); u0 += stride) {
+    float y[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) y[k] = __uint_as_float((uint32_t)(u0 + k));
+    const uint32_t w = e4m3x4_hw(y[0], y[1], y[2], y[3]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t a = (uint32_t)(u0 + k) & 0x7FFFFFFFu;
+      if (a >= 0x43E80000u) continue;                            // |y| >= 464, inf, NaN
+      ++n;
+      bad += ((w >> (8 * k)) & 0xFFu) != f32_to_e4m3_rne(y[k]);
+    }
+  }
+  atomicAdd(counts, bad);
+  atomicAdd(counts + 1, n);
+}
+
+__global__ void zero_u64_kernel(unsigned long long* p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0ull;
+}
+
+hipError_t launch_e4m3_check(unsigned long long* counts, hipStream_t st) {
+  hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(64), 0, st, counts, 2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(e4m3_check_kernel, dim3(4096), dim3(256), 0, st, counts);
+  return hipGetLastError();
 }
 
 hipError_t launch_bridge(const BridgeArgs& a, hipStream_t st) {

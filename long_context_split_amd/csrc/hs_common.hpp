@@ -67,6 +67,16 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_rne(float y) {
   return (u >> 24 & 0x80u) | (uint32_t)mag;
 }
 
+// Four float32 -> four E4M3 codes (byte k from y_k) by the hardware packed conversion
+// (v_cvt_pk_fp8_f32, round to nearest even), a magnitude that rounds to zero stored as +0.  Equal to
+// f32_to_e4m3_rne for every finite |y| < 464 (hs_e4m3_check compares all of them on the device);
+// callers keep |y| below that.
+__device__ __forceinline__ uint32_t e4m3x4_hw(float y0, float y1, float y2, float y3) {
+  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+  w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, (int)w, true);
+  return w & ((((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) & 0x80808080u) | 0x7F7F7F7Fu);
+}
+
 // Order-preserving uint32 key of a float32 (finite values; -0 sorts below +0).
 __device__ __forceinline__ uint32_t f32_key(float x) {
   uint32_t b = __float_as_uint(x);

@@ -248,6 +248,8 @@ static_assert(SELECT_CLAIM_WORD < SELECT_ZERO_WORDS && SELECT_CLAIM_WORD != SELE
 constexpr int SELECT_CAND_MAX_N = 1 << 20;
 hipError_t launch_select_cand(const SelectArgs& a, int n_lists, hipStream_t st);
 hipError_t launch_bridge(const BridgeArgs& a, hipStream_t st);
+// all float32 bit patterns: the bridge's E4M3 conversion against the software RNE (counts: device, 2 words)
+hipError_t launch_e4m3_check(unsigned long long* counts, hipStream_t st);
 // streaming read of bytes (a multiple of 16) with grid workgroups of 512 threads; sink: 16 bytes
 hipError_t launch_read_probe(const void* buf, size_t bytes, int non_temporal, int grid, void* sink, hipStream_t st);
 

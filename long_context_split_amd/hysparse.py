@@ -107,6 +107,8 @@ class hs_kernel_time(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char_p), ("ms", ctypes.c_float)]
 
 
+lib.hs_e4m3_check.restype = ctypes.c_int
+lib.hs_e4m3_check.argtypes = [_P, _P]
 lib.hs_read_probe.restype = ctypes.c_int
 lib.hs_read_probe.argtypes = [_P, ctypes.c_size_t, ctypes.c_int, ctypes.c_int32, _P, _P]
 lib.hs_timing_enable.restype = None
@@ -365,6 +367,15 @@ def read_probe(buf, nbytes=None, non_temporal=True, grid=256, sink=None, stream=
     if sink is None:
         sink = torch.empty(4, dtype=torch.int32, device=buf.device)
     check(lib.hs_read_probe(_ptr(buf), nbytes, 1 if non_temporal else 0, grid, _ptr(sink), _stream(stream)))
+
+
+def e4m3_check(stream=None):
+    """hs_e4m3_check: (mismatches, values compared) of the library's hardware E4M3 conversion against
+    the bit-level RNE reference over every finite float32 with |y| < 464."""
+    counts = torch.empty(2, dtype=torch.int64, device="cuda")
+    check(lib.hs_e4m3_check(_ptr(counts), _stream(stream)))
+    c = counts.cpu().tolist()
+    return int(c[0]), int(c[1])
 
 
 def timing_enable(on=True):

@@ -151,6 +151,12 @@ def test_bridge_rejects(hs):
     assert f(0x900000, 0, 4096, 1, w, w, tp, 0, None) == 0            # nothing to do: no launch
 
 
+def test_e4m3_check_rejects(hs):
+    f = hs.lib.hs_e4m3_check
+    assert f(None, None) == 1
+    assert f(0x900004, None) == 1                                      # not 8-byte aligned
+
+
 def test_append_rejects(hs):
     t = _cache(hs, dtype=2, scales=True, lens=(1,), cap=1000)
     tp = (ctypes.POINTER(hs.hs_kv_cache) * 1)(ctypes.pointer(t))

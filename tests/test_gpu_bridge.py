@@ -45,6 +45,19 @@ def _untouched(arr, r0, r1, sentinel):
     return np.all(arr[:r0] == sentinel) and np.all(arr[r1:] == sentinel)
 
 
+def test_hardware_e4m3_conversion_equals_rne_reference():
+    """The bridge stores E4M3 codes with the hardware packed conversion.  On this device it gives the
+    bit-level round-to-nearest-even code (zero magnitudes as +0, saturation at 448) for every finite
+    float32 below 464 in magnitude, 2 x 0x43E80000 values; the bit-level reference itself matches the
+    oracle's encoder in the bridge and append tests here."""
+    from long_context_split_amd import hysparse as hs
+    banner("E4M3 hardware conversion, every float32 |y| < 464")
+    bad, n = hs.e4m3_check()
+    assert n == 2 * 0x43E80000
+    assert bad == 0
+    print(f"[result] e4m3 hardware conversion: {bad} mismatches over {n} values", flush=True)
+
+
 @pytest.mark.parametrize("fp8", [True, False])
 def test_identity_weights_bit_exact(fp8):
     banner(f"bridge identity W fp8={fp8}")
