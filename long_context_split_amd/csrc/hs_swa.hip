@@ -14,9 +14,10 @@
 // current one is used), stored in LDS as bf16 [token][d] for K and V (E4M3 converted on the way),
 // and every wave applies its own band as a mask.  S^T = K Q^T and O^T += V^T P^T run on bf16 MFMA
 // with an online softmax in log2 units; the V^T operand comes from two LDS transpose reads (4 rows
-// each, the token order of the P operand).  The output goes straight from the accumulators.
+// each, the token order of the P operand).
 // Bands overlap between neighbouring workgroups too, so K/V rows come mostly from L2; the kernel's
-// HBM traffic is Q in and O out.
+// HBM traffic is Q in and O out.  O leaves through a per-wave LDS staging area as whole 128-byte pieces
+// of head rows.
 
 #include "hs_common.hpp"
 #include "hs_internal.hpp"
@@ -29,6 +30,7 @@ namespace {
 constexpr int SKROW = 272;                         // K tile row: 256 B + 16 B pad (16-byte operand reads)
 constexpr int SVROW = 288;                         // V tile row: 256 B + 32 B pad (4-row transpose reads)
 constexpr int SBUF = 32 * SKROW + 32 * SVROW;      // one tile: K then V (bf16)
+constexpr int OPITCH = 36;                         // output staging: floats per head row (32 d + 4 pad)
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -50,7 +52,8 @@ __global__ __launch_bounds__(64 * NW) void swa_attn_kernel(AttnArgs a) {
   constexpr int PPR = SB / 16;                      // 16-byte pieces per row
   constexpr int PPT = 2 * 32 * PPR / NT;            // 16-byte pieces per thread per tile (K and V)
   static_assert(PPT >= 1 && PPT * NT == 2 * 32 * PPR, "a tile's K and V pieces split evenly over the threads");
-  __shared__ __align__(16) char smem[2 * SBUF];
+  constexpr int SMEM = 2 * SBUF > NW * 32 * OPITCH * 4 ? 2 * SBUF : NW * 32 * OPITCH * 4;
+  __shared__ __align__(16) char smem[SMEM];
   __shared__ float scl[2][2][32];                   // per buffer: K scale x softmax scale, V scale (E4M3)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -200,17 +203,31 @@ __global__ __launch_bounds__(64 * NW) void swa_attn_kernel(AttnArgs a) {
   }
   if (!active) return;
   lsum += __shfl_xor(lsum, 32);
-  const int gh = hb * 32 + tok;
-  if (gh >= a.G) return;
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  float* const orow = a.out + (((size_t)b * a.n_q + i) * a.H + (size_t)g * a.G + gh) * D;
+  // ---- output: for each block of 32 d, the wave's 32 heads x 32 d go through its own LDS area (the
+  // tiles are dead after the loop's last barrier) and leave as whole 128-byte pieces of head rows
+  float* const ob = (float*)smem + wave * (32 * OPITCH);
+  const int nh = min(32, a.G - hb * 32);                          // heads of this block that exist
+  float* const obase = a.out + (((size_t)b * a.n_q + i) * a.H + (size_t)g * a.G + hb * 32) * D;
 #pragma unroll
-  for (int mt4 = 0; mt4 < 4; ++mt4)
+  for (int mt4 = 0; mt4 < 4; ++mt4) {
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const f32x4 o = {acc[mt4][4 * r4], acc[mt4][4 * r4 + 1], acc[mt4][4 * r4 + 2], acc[mt4][4 * r4 + 3]};
-      *(f32x4*)(orow + 32 * mt4 + crow(lane, 4 * r4)) = o * inv;
+      *(f32x4*)(ob + tok * OPITCH + crow(lane, 4 * r4)) = o * inv;
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {                                 // head 8 k + lane / 8, d quad lane % 8
+      const int hd = 8 * k + (lane >> 3), pc = lane & 7;
+      if (hd < nh) *(f32x4*)(obase + (size_t)hd * D + 32 * mt4 + 4 * pc) = *(const f32x4*)(ob + hd * OPITCH + 4 * pc);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");        // reads done before the next block's writes
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
 }
 
 template <int KVT>

@@ -41,7 +41,9 @@ def test_swa_parity(kvtype, lens, n_kv, H, n_q, w):
     banner(f"swa {kvtype} lens={lens} n_kv={n_kv} H={H} n_q={n_q} w={w}")
     from long_context_split_amd import hysparse as hs
     up = _case(kvtype, lens, n_kv, H, n_q, seed=len(lens) * 1000 + w + H)
-    out = hs.swa_attn(up.kv, up.q_full, w)
+    B, nq, Hq, _ = up.q_full.shape
+    poison = torch.full((B, nq, Hq, 128), float("nan"), dtype=torch.float32, device="cuda")
+    out = hs.swa_attn(up.kv, up.q_full, w, out=poison)     # every element must be written
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     tol = 2e-3 if kvtype == "bf16" else 3e-2
