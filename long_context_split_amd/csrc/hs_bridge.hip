@@ -11,7 +11,8 @@
 //
 // Workgroup tile: 256 tokens x 256 columns (one target: K's 128 columns, then V's), K-stage 64, 8 waves
 // each owning 64 rows x 128 columns = one head block, so a row's amax is reduced inside one wave; one
-// workgroup per CU.  The stages are double-buffered in LDS (one barrier per stage) and the global loads
+// workgroup per CU.  Chunks too short to give every CU a 256-token tile (a prefill chunk of 8192
+// tokens with 4 targets makes 128) take 128-token tiles, 32 rows per wave.  The stages are double-buffered in LDS (one barrier per stage) and the global loads
 // run two stages ahead in two register buffers.  MFMA v_mfma_f32_32x32x16_bf16 with operands from LDS:
 // A = rows of X (16-byte reads, 144-byte row pitch); W is kept in its own [k][column] layout (576-byte
 // row pitch) and each B operand (8 consecutive k of one column) comes from two LDS transpose reads,
@@ -31,14 +32,11 @@
 namespace hs {
 
 namespace {
-constexpr int BM = 256, BN = 256, BK = 64, NT = 512;
+constexpr int BN = 256, BK = 64, NT = 512;
 constexpr int AROW = BK * 2 + 16;               // 144 B per X row in LDS
 constexpr int WROW = 576;                       // bytes per k row of W (256 columns) in LDS
-constexpr int STAGE = BM * AROW + BK * WROW;
-constexpr int SMEM = 2 * STAGE;
-constexpr int APT = BM * BK * 2 / 16 / NT;      // X pieces per thread per stage (4)
 constexpr int BPT = BK * BN * 2 / 16 / NT;      // W pieces per thread per stage (4)
-static_assert(APT == 4 && BPT == 4, "load split");
+static_assert(BPT == 4, "load split");
 
 __device__ __forceinline__ int crow(int lane, int r) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
@@ -49,11 +47,17 @@ __device__ __forceinline__ u32x2 read_tr(const char* p) {      // LDS transpose 
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p)));
 }
 
-struct Regs { u32x4 a[APT], b[BPT]; };
+template <int APT> struct Regs { u32x4 a[APT], b[BPT]; };
 }  // namespace
 
+// BM = 256 tokens per workgroup (8 waves of 64 rows x 128 columns), or 128 (32 rows each) when the
+// 256-token tiles would leave CUs idle
+template <int BM>
 __global__ __launch_bounds__(NT) void bridge_kernel(BridgeArgs a) {
-  __shared__ __align__(16) char smem[SMEM];
+  constexpr int STAGE = BM * AROW + BK * WROW;
+  constexpr int APT = BM * BK * 2 / 16 / NT;                     // X pieces per thread per stage (4 or 2)
+  constexpr int RW = BM / 4, NI = RW / 32;                        // rows per wave, its 32-row blocks
+  __shared__ __align__(16) char smem[2 * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   // tile order: groups of 8 token tiles x all targets are consecutive in dispatch order (x fastest), and
@@ -73,7 +77,7 @@ __global__ __launch_bounds__(NT) void bridge_kernel(BridgeArgs a) {
   const int Dm = a.Dm;
   const int S = Dm / BK;                                          // stages (>= 1)
 
-  auto load = [&](Regs& r, int s) {                               // stage s; past the last: stage S - 1 again
+  auto load = [&](Regs<APT>& r, int s) {                               // stage s; past the last: stage S - 1 again
     const int k0 = min(s, S - 1) * BK;
 #pragma unroll
     for (int i = 0; i < APT; ++i) {
@@ -87,7 +91,7 @@ __global__ __launch_bounds__(NT) void bridge_kernel(BridgeArgs a) {
       r.b[i] = *(const u32x4*)((c < 16 ? wk : wv) + (int64_t)(k0 + kr) * D + (c & 15) * 8);
     }
   };
-  auto store = [&](const Regs& r, int buf) {
+  auto store = [&](const Regs<APT>& r, int buf) {
     char* const As = smem + buf * STAGE;
     char* const Bs = As + BM * AROW;
 #pragma unroll
@@ -101,16 +105,16 @@ __global__ __launch_bounds__(NT) void bridge_kernel(BridgeArgs a) {
       *(u32x4*)(Bs + (p >> 5) * WROW + (p & 31) * 16) = r.b[i];
     }
   };
-  f32x16 acc[2][4] = {};
+  f32x16 acc[NI][4] = {};
   auto compute = [&](int buf) {
     const char* const As = smem + buf * STAGE;
     const char* const Bs = As + BM * AROW;
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
-      s16x8 av[2], bv[4];
+      s16x8 av[NI], bv[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        av[i] = *(const s16x8*)(As + (64 * wm + 32 * i + (lane & 31)) * AROW + (16 * s + 8 * (lane >> 5)) * 2);
+      for (int i = 0; i < NI; ++i)
+        av[i] = *(const s16x8*)(As + (RW * wm + 32 * i + (lane & 31)) * AROW + (16 * s + 8 * (lane >> 5)) * 2);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {                               // k = 16 s + 8 (lane >> 5) + 0..7, column 128 wn + 32 j + (lane & 31)
         const char* p = Bs + (16 * s + 8 * (lane >> 5) + ((lane & 15) >> 2)) * WROW +
@@ -120,7 +124,7 @@ __global__ __launch_bounds__(NT) void bridge_kernel(BridgeArgs a) {
         bv[j] = __builtin_bit_cast(s16x8, q);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[i]),
@@ -134,7 +138,7 @@ __global__ __launch_bounds__(NT) void bridge_kernel(BridgeArgs a) {
   // alternate (the loop handles two stages per pass, so each wait is a static count); loads past the
   // last stage re-read it; storing them (unconditionally: a branch around the store would make the
   // compiler wait for every load in flight) writes a buffer no later stage reads.
-  Regs r0, r1;
+  Regs<APT> r0, r1;
   load(r0, 0);
   load(r1, 1);
   store(r0, 0);
@@ -152,12 +156,12 @@ __global__ __launch_bounds__(NT) void bridge_kernel(BridgeArgs a) {
     __syncthreads();
   }
 
-  // ---- epilogue: this wave holds rows 64 wm + [0, 64) of head block (tgt, wn), all in registers.
+  // ---- epilogue: this wave holds rows RW wm + [0, RW) of head block (tgt, wn), all in registers.
   // Lane l holds, for rows 32 i + crow(l, r), the columns 32 j + (l & 31), j = 0..3.  Within a quad of
   // lanes 4 m + t, a byte (or bf16) transpose leaves lane 4 m + t with columns 32 t + 4 m .. + 3 of the
   // row, so one store per (i, r) writes two whole rows (lanes 0..31 one row, 32..63 the other).
   const int blk = 2 * tgt + wn;
-  const int64_t t0 = m0 + 64 * wm;                              // first token of this wave's rows
+  const int64_t t0 = m0 + RW * wm;                              // first token of this wave's rows
   auto orow = [&](int rl) -> int64_t { return a.rows ? a.rows[t0 + rl] : a.row_offset + t0 + rl; };
   char* const dst = (char*)a.out[blk];
   const int qt = lane & 3, qm = (lane & 31) >> 2;
@@ -175,7 +179,7 @@ __global__ __launch_bounds__(NT) void bridge_kernel(BridgeArgs a) {
   if (a.fp8) {
     float* const sc = a.scale[blk];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NI; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float am = 0.f;
@@ -202,7 +206,7 @@ __global__ __launch_bounds__(NT) void bridge_kernel(BridgeArgs a) {
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NI; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         // p01 = bf16 of tiles (0, 1), p23 = tiles (2, 3); lane 4 m + t takes tile t of quad lanes 0..3
@@ -263,8 +267,14 @@ hipError_t launch_e4m3_check(unsigned long long* counts, hipStream_t st) {
 }
 
 hipError_t launch_bridge(const BridgeArgs& a, hipStream_t st) {
-  dim3 grid((unsigned)((a.T + BM - 1) / BM), a.n_targets);
-  hipLaunchKernelGGL(bridge_kernel, grid, dim3(NT), 0, st, a);
+  // 256-token tiles while they give every CU a workgroup, else 128-token tiles (twice the workgroups)
+  if ((a.T + 255) / 256 * a.n_targets >= 256) {
+    dim3 grid((unsigned)((a.T + 255) / 256), a.n_targets);
+    hipLaunchKernelGGL(bridge_kernel<256>, grid, dim3(NT), 0, st, a);
+  } else {
+    dim3 grid((unsigned)((a.T + 127) / 128), a.n_targets);
+    hipLaunchKernelGGL(bridge_kernel<128>, grid, dim3(NT), 0, st, a);
+  }
   return hipGetLastError();
 }
 

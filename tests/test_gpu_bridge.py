@@ -154,6 +154,33 @@ def test_tile_order_with_partial_group(T, nt):
     print(f"[result] bridge T={T} targets={nt} equal fraction {frac:.5f}", flush=True)
 
 
+@pytest.mark.parametrize("fp8", [True, False])
+def test_token_tile_sizes_agree(fp8):
+    """16384 tokens x 4 targets make 256 workgroups of 256-token tiles; 16128 tokens (252) take the
+    128-token tiles.  Each output row is the same K-ordered sum either way, so the rows both calls
+    store are bit-identical; the 16128-token call is also checked against the oracle."""
+    banner(f"bridge tile sizes T=16384 vs 16128 D=512 targets=4 fp8={fp8}")
+    from long_context_split_amd import hysparse as hs
+    case = synth.bridge_case(4, T=16384, D=512, n_targets=4)
+    x = dev_bf16(case["x"])
+    wk, wv = [dev_bf16(w) for w in case["w_k"]], [dev_bf16(w) for w in case["w_v"]]
+    big, small = _targets(4, 16384, fp8), _targets(4, 16384, fp8)
+    hs.kv_bridge(x, wk, wv, big, 0)
+    hs.kv_bridge(x[:16128].contiguous(), wk, wv, small, 0)
+    torch.cuda.synchronize()
+    for tb, ts in zip(big, small):
+        assert torch.equal(tb.k.view(torch.uint8)[:16128], ts.k.view(torch.uint8)[:16128])
+        assert torch.equal(tb.v.view(torch.uint8)[:16128], ts.v.view(torch.uint8)[:16128])
+        if fp8:
+            assert torch.equal(tb.k_scale[:16128], ts.k_scale[:16128]) and torch.equal(tb.v_scale[:16128], ts.v_scale[:16128])
+        rest = ts.k.view(torch.uint8)[16128:] if fp8 else ts.k.view(torch.int16)[16128:]
+        assert torch.equal(rest, torch.full_like(rest, SENT8 if fp8 else 0x1234))      # rows past T untouched
+    sub = dict(case, T=16128, x=case["x"][:16128])
+    frac = _check_random(sub, small, 0, fp8)
+    assert frac >= 0.99
+    print(f"[result] bridge tile sizes fp8={fp8}: bit-identical rows, oracle equal fraction {frac:.5f}", flush=True)
+
+
 @pytest.mark.parametrize("D,fp8", [(64, True), (192, True), (192, False), (320, True)])
 def test_odd_stage_counts(D, fp8):
     """d_model 64, 192, 320: 1, 3 and 5 K-stages of 64, so the stage loop leaves through its odd exit
