@@ -546,6 +546,26 @@ def bench_bridge(dev, iters):
     out_bytes = nt * 2 * T * (128 + 4)
     in_bytes = T * D * 2 + nt * 2 * D * 128 * 2
     log(f"bridge: {ms * 1e3:.1f} us  {tflops:.1f} TFLOP/s  ({tflops / 2500.0:.3f} of bf16 MFMA peak)")
+    # context, not the product path: the same product as one plain library GEMM (torch.matmul, i.e.
+    # hipBLASLt) with a bf16 output and no storage epilogue, with the weights in the layout the bridge
+    # takes ([d_model, columns]) and pre-transposed ([columns, d_model])
+    wcat = torch.cat([w for pair in zip(wk, wv) for w in pair], dim=1).contiguous()      # [D, nt * 2 * 128]
+    wcat_t = wcat.t().contiguous()
+    lib = {}
+    for name, f in (("w_dm_major", lambda: torch.matmul(x, wcat)), ("w_col_major", lambda: torch.matmul(x, wcat_t.t()))):
+        for _ in range(2):
+            f()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        for a, b in evs:
+            a.record()
+            f()
+            b.record()
+        torch.cuda.synchronize()
+        lms = statistics.median(a.elapsed_time(b) for a, b in evs)
+        lib[name] = {"us": round(lms * 1e3, 1), "tflops": round(flops / (lms * 1e-3) / 1e12, 1)}
+    del wcat, wcat_t
+    log(f"library GEMM (torch.matmul, bf16 out, no epilogue): {lib}")
     # decode-time append: one new token per sequence of a 32-sequence batch, same weights and targets,
     # each token to its own cache row
     nb = 32
@@ -576,6 +596,8 @@ def bench_bridge(dev, iters):
     return {"workload": "c4_bridge_32k: X[32768,4096] bf16 x 4 targets (K,V) -> FP8 E4M3 + per-token scale",
             "ms": round(ms, 4), "tflops": round(tflops, 1), "bound": "mfma", "peak_tflops": 2500.0,
             "frac": round(tflops / 2500.0, 4), "flops": flops, "bytes": in_bytes + out_bytes,
+            "library_gemm": {"what": "torch.matmul (hipBLASLt) of the same X and the 8 weight matrices "
+                                     "concatenated, bf16 output, no storage epilogue; context only", **lib},
             "decode_append": {"workload": f"{nb} new tokens x 4096 -> 4 targets (K,V), FP8, scattered rows",
                               "us": round(ms_app * 1e3, 2), "bytes": app_bytes,
                               "GBps": round(app_bytes / (ms_app * 1e-3) / 1e9, 1), "bound": "hbm (weights)"}}

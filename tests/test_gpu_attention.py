@@ -330,16 +330,16 @@ def test_determinism_bitwise():
 
 
 @pytest.mark.slow
-def test_config2_full_size_sampled():
+def test_config2_full_size():
     """Config 2 at full size in the benchmark's launch configuration: 32 sequences
     of 131072 rows, bf16, 64 needles each, 1 full + 5 sparse layers.  Oracle on
-    sampled sequences; needles checked on all of them."""
+    every sequence (outputs, LSE, scores, lists, recall, sparse layers); needles."""
     banner("config 2 full size: B=32 L=131072 H=32 bf16")
     up = Uploaded(synth.decode_case(2))
     res = _run_block(up)
     _same_lists_without_scores(up, res)
     stats = {}
-    for i in (0, 17, 31):
+    for i in range(32):
         banner(f"config 2 oracle on sequence {i}")
         _check_seq(up, res, i, stats=stats)
     assert stats["hit"] / stats["tot"] >= 0.999
@@ -364,18 +364,18 @@ def test_config3_full_size():
 
 
 @pytest.mark.slow
-def test_config5_full_size_sampled():
+def test_config5_full_size():
     """Config 5 at full size in the benchmark's launch configuration: 8 ragged sequences of
-    64K-512K rows, bf16, H=32, 1 full + 5 sparse layers per block, each block with its own cache.
-    Blocks 0 and 3 run; the oracle checks each one's shortest and longest sequence."""
+    64K-512K rows, bf16, H=32, 1 full + 5 sparse layers per block, each of the 4 blocks with its
+    own cache and queries.  The oracle checks every sequence of every block."""
     stats = {}
-    for blk in (0, 3):
+    for blk in range(4):
         banner(f"config 5 full size: block {blk}")
         up = Uploaded(synth.decode_case(5, block=blk))
         res = _run_block(up)
         _same_lists_without_scores(up, res)
         lens = up.case["lengths"]
-        for i in (int(np.argmin(lens)), int(np.argmax(lens))):
+        for i in range(len(lens)):
             banner(f"config 5 block {blk}: oracle on sequence {i} (L={int(lens[i])})")
             _check_seq(up, res, i, stats=stats)
         del up, res
