@@ -29,7 +29,7 @@ METRIC = "hybrid-block decode queries/s + achieved HBM GB/s at 128K–1M ctx, 1 
 # HBM bytes per launch of the dense split-K pass at the default workload, from two
 # rocprofv3 --pmc runs (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors read off a
 # plain 1 GiB copy), keyed by a digest of the kernel sources they were taken on.
-KNOWN_TRAFFIC = {"aae4fee290a74b3a": 2305921331}
+KNOWN_TRAFFIC = {"311812f75142137b": 2305919388}
 KERNEL_SOURCES = ["long_context_split_amd/csrc/hs_wave.hip", "long_context_split_amd/csrc/hs_mfma.hpp",
                   "long_context_split_amd/csrc/hs_common.hpp", "long_context_split_amd/csrc/hs_internal.hpp"]
 
@@ -296,7 +296,8 @@ def main():
         "config": {
             "workload": (spec["name"] if args.L is None and args.B is None else
                          f"{spec['name']}_L{args.L or 'cfg'}_B{args.B or 'cfg'}") +
-                        (f"_block{args.select_block}" if args.select_block else ""),
+                        (f"_block{args.select_block}" if args.select_block else "") +
+                        "".join(f"_{k.lower()}{v}" for k, v in sorted(os.environ.items()) if k.startswith("HS_")),
             "batch": B, "seq_len": int(lens.max()) if args.config == 2 else [int(x) for x in lens],
             "query_heads": H, "kv_heads": 1, "head_dim": 128, "q_tokens": n_q, "top_k": top_k, "window": window,
             "sparse_layers": n_sparse, "blocks": n_blocks, "kv_dtype": spec["kv"],

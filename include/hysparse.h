@@ -209,7 +209,12 @@ hs_status hs_kv_append(const void *hidden, int64_t n_tokens, int32_t d_model, in
  * Errors: HS_ERR_INVALID_ARGUMENT (null pointer, misaligned pointer, bad shape,
  * L_b < 1, rows outside capacity, scale pointers not matching the dtype,
  * top_k/window < 0), HS_ERR_WORKSPACE_TOO_SMALL, HS_ERR_UNSUPPORTED (head_dim !=
- * 128, another G, more than 65535 lists B * q_tokens * num_kv_heads). */
+ * 128, another G, more than 65535 lists B * q_tokens * num_kv_heads).
+ * Opt-in, E4M3 caches with more than 32 query rows per KV head: with the environment
+ * variable HS_MANY_ROW_FP8_QK=1 (read at each call) the products q.k of out and lse use q
+ * rounded to E4M3 per query row (scale = that row's amax / 448) on FP8 matrix units; the
+ * selection scores still use the bf16 q, but with that lse.  This changes the results and
+ * is off by default. */
 hs_status hs_full_attn_select(const hs_kv_cache *kv, const hs_attn_params *p, const void *q,
                               hs_dtype q_dtype, float *out, float *lse, int32_t *sel_idx,
                               int32_t *sel_count, float *scores_out, void *workspace,

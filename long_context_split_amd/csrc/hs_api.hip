@@ -662,8 +662,11 @@ hs_status hs_full_attn_select(const hs_kv_cache* kv, const hs_attn_params* p, co
   hipError_t e;
   if (pl.wave)
     e = timed("attn_wave_dense", s, [&] { return hs::launch_attn_wave(a, kvt, s); });
-  else if (pl.rows)
+  else if (pl.rows) {
+    // opt-in: Q K^T of the many-row pass on FP8 MFMA for E4M3 caches (Q quantised per row)
+    a.qk_fp8 = kvt == hs::KV_FP8 && env_int("HS_MANY_ROW_FP8_QK", 0) != 0;
     e = timed("attn_rows_dense", s, [&] { return hs::launch_attn_rows(a, kvt, pl.nrg, s); });
+  }
   else
     e = timed("attn_partial_dense", s, [&] { return hs::launch_attn_partial(a, kvt, pl.ct, pl.nwr, false, s); });
   if (e != hipSuccess) return hip_fail(e, "full attention pass 1");

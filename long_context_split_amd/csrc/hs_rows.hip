@@ -1,4 +1,5 @@
-// Full-attention pass 1 for many query rows per KV head (gfx950, bf16 MFMA).
+// Full-attention pass 1 for many query rows per KV head (gfx950, bf16 MFMA; for E4M3 caches an
+// opt-in form takes Q K^T on FP8 MFMA, see QK8 below).
 //
 // ithome page "小米公开 MiMo-V3 核心架构 HySparse2", section "KV Reuse": the full
 // layer attends over every cached row of the sequence; with several query
@@ -37,6 +38,8 @@ namespace hs {
 
 namespace {
 
+typedef int v8i32 __attribute__((ext_vector_type(8)));
+
 // position of token o (0..15) inside its 16-token group of the V^T tile
 __device__ __forceinline__ int vt_col(int tok) {
   const int o = tok & 15;
@@ -50,8 +53,13 @@ __device__ __forceinline__ int vt_quad(int d, int q) { return (q ^ ((2 * (d >> 4
 
 }  // namespace
 
-template <int KVT, int NRG>
+// QK8 (E4M3 caches only): S^T = K Q^T on FP8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4, unit block
+// scales): K stays as its E4M3 codes in LDS, Q is quantised to E4M3 per query row (scale = the row's
+// amax / 448, round to nearest even) and both scales multiply the raw products inside exp2's fma.
+// The V side, the softmax and the outputs are as in the bf16 form.
+template <int KVT, int NRG, bool QK8>
 __global__ __launch_bounds__(64 * NRG) void attn_rows_kernel(AttnArgs a) {
+  static_assert(!QK8 || KVT == KV_FP8, "FP8 products need an E4M3 cache");
   constexpr int NT = 64 * NRG;
   constexpr int TT = NRG >= 4 ? 128 : 64;                        // tokens per super-tile
   constexpr int NSUB = TT / 32;
@@ -62,7 +70,7 @@ __global__ __launch_bounds__(64 * NRG) void attn_rows_kernel(AttnArgs a) {
   constexpr int EPP = FP8 ? 16 : 8;                              // elements per piece
   constexpr int PPT = TT * PPR / NT;                             // pieces per thread per tensor
   static_assert(TT * PPR % NT == 0, "super-tile pieces split evenly over the threads");
-  constexpr int KROW = 272;                                      // K tile: 256 B + 16 pad
+  constexpr int KROW = QK8 ? 144 : 272;                         // K tile: 128 codes or 256 B of bf16, + 16 pad
   constexpr int VROW = TT * 2 + 16;                              // V^T tile row: TT tokens + 16 pad
   __shared__ __align__(16) char kt[TT * KROW];
   __shared__ __align__(16) char vt[D * VROW];
@@ -108,11 +116,48 @@ __global__ __launch_bounds__(64 * NRG) void attn_rows_kernel(AttnArgs a) {
   const int row = blockIdx.z * 32 * NRG + 32 * wave + (lane & 31);
   const bool row_ok = row < a.R;
   Mma<CT_BF16>::QOp q;
+  v8i32 q8[2];                                                    // QK8: E4M3 Q operand, k-step kk holds
+  float qs = 1.f;                                                 // d = 64 kk + 32 (lane >> 5) + byte
   {
     const int t = row_ok ? row / a.G : 0, hh = row_ok ? row % a.G : 0;
     const size_t qoff = (((size_t)b * a.n_q + t) * a.H + (size_t)g * a.G + hh) * D;
     const void* qrow = a.q_f32 ? (const void*)((const float*)a.q + qoff) : (const void*)((const uint16_t*)a.q + qoff);
-    Mma<CT_BF16>::load_q(q, qrow, a.q_f32, row_ok, lane);
+    if constexpr (QK8) {
+      float x[64];                                                // x[32 kk + j]: d = 64 kk + 32 (lane >> 5) + j
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int d0 = 64 * kk + 32 * (lane >> 5);
+        if (a.q_f32) {
+#pragma unroll
+          for (int j = 0; j < 32; ++j) x[32 * kk + j] = row_ok ? ((const float*)qrow)[d0 + j] : 0.f;
+        } else {
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const u32x4 w = row_ok ? *(const u32x4*)((const uint16_t*)qrow + d0 + 8 * h) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              x[32 * kk + 8 * h + 2 * e] = __uint_as_float(w[e] << 16);
+              x[32 * kk + 8 * h + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+            }
+          }
+        }
+      }
+      float am = 0.f;
+#pragma unroll
+      for (int j = 0; j < 64; ++j) am = fmaxf(am, fabsf(x[j]));
+      am = fmaxf(am, __shfl_xor(am, 32));                         // the row's other 64 d
+      qs = am / 448.0f;
+      if (qs == 0.f) qs = 1.f;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const float* y = x + 32 * kk + 4 * w;
+          q8[kk][w] = (int)e4m3x4_hw(y[0] / qs, y[1] / qs, y[2] / qs, y[3] / qs);
+        }
+    } else {
+      Mma<CT_BF16>::load_q(q, qrow, a.q_f32, row_ok, lane);
+    }
   }
 
   float m = -INFINITY, lsum = 0.f;
@@ -138,17 +183,21 @@ __global__ __launch_bounds__(64 * NRG) void attn_rows_kernel(AttnArgs a) {
         if constexpr (FP8) {
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            e4m3x4_to_bf16x4(xk[w], kw[t2][2 * w], kw[t2][2 * w + 1]);
+            if (!QK8) e4m3x4_to_bf16x4(xk[w], kw[t2][2 * w], kw[t2][2 * w + 1]);
             e4m3x4_to_bf16x4(xv[w], vw[t2][2 * w], vw[t2][2 * w + 1]);
           }
         } else {
 #pragma unroll
           for (int w = 0; w < 4; ++w) { kw[t2][w] = xk[w]; vw[t2][w] = xv[w]; }
         }
-        char* kd = kt + (m2 + t2) * KROW + c * (2 * EPP);
+        if constexpr (QK8) {
+          *(u32x4*)(kt + (m2 + t2) * KROW + c * 16) = xk;           // the row's codes, d order
+        } else {
+          char* kd = kt + (m2 + t2) * KROW + c * (2 * EPP);
 #pragma unroll
-        for (int h = 0; h < EPP / 8; ++h)
-          *(u32x4*)(kd + 16 * h) = u32x4{kw[t2][4 * h], kw[t2][4 * h + 1], kw[t2][4 * h + 2], kw[t2][4 * h + 3]};
+          for (int h = 0; h < EPP / 8; ++h)
+            *(u32x4*)(kd + 16 * h) = u32x4{kw[t2][4 * h], kw[t2][4 * h + 1], kw[t2][4 * h + 2], kw[t2][4 * h + 3]};
+        }
       }
       const int col = vt_col(m2);                                 // even; token m2 + 1 is at col + 1
 #pragma unroll
@@ -190,7 +239,15 @@ __global__ __launch_bounds__(64 * NRG) void attn_rows_kernel(AttnArgs a) {
         for (int u = 0; u < 2; ++u)
           va[mt4][u] = *(const s16x8*)((u ? vb1 : vb0) + mt4 * 32 * VROW + 64 * (st ^ (mt4 & (NSUB - 1))));
       f32x16 s = {};
-      {
+      if constexpr (QK8) {                                          // A: the token's codes d = 64 kk + 32 (lane >> 5) + 0..31
+        const char* kb = kt + (32 * st + (lane & 31)) * KROW + (lane >> 5) * 32;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const u32x4 lo = *(const u32x4*)(kb + 64 * kk), hi = *(const u32x4*)(kb + 64 * kk + 16);
+          const v8i32 ka = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, q8[kk], s, 0, 0, 0, 0, 0, 0);
+        }
+      } else {
         const char* kb = kt + (32 * st + (lane & 31)) * KROW + (lane >> 5) * 16;
 #pragma unroll
         for (int k8 = 0; k8 < 8; ++k8) {
@@ -209,7 +266,7 @@ __global__ __launch_bounds__(64 * NRG) void attn_rows_kernel(AttnArgs a) {
 #pragma unroll
       for (int r = 1; r < 16; ++r) smax = fmaxf(smax, s[r]);
       smax = fmaxf(smax, __shfl_xor(smax, 32));
-      const float mt = smax * (smax >= 0.f ? fmax_t : fmin_t);      // >= the tile's max logit (log2 units)
+      const float mt = smax * (smax >= 0.f ? fmax_t : fmin_t) * qs; // >= the tile's max logit (log2 units)
       const bool need = mt > m + TAU;                               // same for both lanes of a row
       if (__ballot(need)) {
         const float mn = need ? mt : m;
@@ -227,6 +284,7 @@ __global__ __launch_bounds__(64 * NRG) void attn_rows_kernel(AttnArgs a) {
         if (FP8) {
           f = *(const f32x4*)(ksc + t0);
           v4 = *(const f32x4*)(vsc + t0);
+          if (QK8) f *= qs;                                         // the row's Q scale
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -440,20 +498,20 @@ static hipError_t launch_rows_scores_t(const ScoreArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int KVT, int NRG>
+template <int KVT, int NRG, bool QK8>
 static hipError_t launch_rows_t(const AttnArgs& a, hipStream_t st) {
   const int z = (a.R + 32 * NRG - 1) / (32 * NRG);
   dim3 grid(a.max_chunks, a.n_lists, z);
-  hipLaunchKernelGGL((attn_rows_kernel<KVT, NRG>), grid, dim3(64 * NRG), 0, st, a);
+  hipLaunchKernelGGL((attn_rows_kernel<KVT, NRG, QK8>), grid, dim3(64 * NRG), 0, st, a);
   return hipGetLastError();
 }
 
-template <int KVT>
+template <int KVT, bool QK8>
 static hipError_t launch_rows_k(const AttnArgs& a, int nrg, hipStream_t st) {
   switch (nrg) {
-    case 2: return launch_rows_t<KVT, 2>(a, st);
-    case 4: return launch_rows_t<KVT, 4>(a, st);
-    default: return launch_rows_t<KVT, 8>(a, st);
+    case 2: return launch_rows_t<KVT, 2, QK8>(a, st);
+    case 4: return launch_rows_t<KVT, 4, QK8>(a, st);
+    default: return launch_rows_t<KVT, 8, QK8>(a, st);
   }
 }
 
@@ -476,8 +534,8 @@ hipError_t launch_attn_rows_scores(const ScoreArgs& a, int kvt, int nrg, hipStre
 }
 
 hipError_t launch_attn_rows(const AttnArgs& a, int kvt, int nrg, hipStream_t st) {
-  if (kvt == KV_BF16) return launch_rows_k<KV_BF16>(a, nrg, st);
-  if (kvt == KV_FP8) return launch_rows_k<KV_FP8>(a, nrg, st);
+  if (kvt == KV_BF16) return launch_rows_k<KV_BF16, false>(a, nrg, st);
+  if (kvt == KV_FP8) return a.qk_fp8 ? launch_rows_k<KV_FP8, true>(a, nrg, st) : launch_rows_k<KV_FP8, false>(a, nrg, st);
   return hipErrorInvalidValue;
 }
 
