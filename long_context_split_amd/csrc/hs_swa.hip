@@ -8,8 +8,10 @@
 // sits at position p = L_b - n_q + i and attends to rows max(0, p - w + 1) .. p of its own cache,
 // the softmax taken over that band.
 //
-// One wave per query token and block of 32 query heads of one KV head, 8 waves (8 consecutive
-// tokens) per workgroup.  The 8 bands overlap almost entirely, so the workgroup walks their union
+// One wave per query token and block of 32 query heads of one KV head, 4 waves (4 consecutive
+// tokens) per workgroup and two workgroups per CU (at most 256 VGPRs per wave), so one workgroup's
+// Q loads, first tiles and output stores overlap the other's tile work.  The 4 bands overlap
+// almost entirely, so the workgroup walks their union
 // in 32-row tiles: each tile is loaded once by all threads (next tile in registers while the
 // current one is used), stored in LDS as bf16 [token][d] for K and V (E4M3 converted on the way),
 // and every wave applies its own band as a mask.  S^T = K Q^T and O^T += V^T P^T run on bf16 MFMA
@@ -44,7 +46,7 @@ __device__ __forceinline__ u32x2 read_tr(const char* p) {
 }  // namespace
 
 template <int KVT, int NW>
-__global__ __launch_bounds__(64 * NW) void swa_attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * NW, 2) void swa_attn_kernel(AttnArgs a) {
   constexpr int NT = 64 * NW;
   constexpr bool FP8 = KVT == KV_FP8;
   constexpr bool SPLIT = !FP8;                      // bf16 cache: P as bf16 hi + lo
@@ -232,7 +234,7 @@ __global__ __launch_bounds__(64 * NW) void swa_attn_kernel(AttnArgs a) {
 
 template <int KVT>
 static hipError_t launch_swa_t(const AttnArgs& a, hipStream_t st) {
-  constexpr int NW = 8;
+  constexpr int NW = 4;                             // tokens per workgroup (two workgroups per CU)
   dim3 grid((a.n_q + NW - 1) / NW, a.n_lists, (a.G + 31) / 32);
   hipLaunchKernelGGL((swa_attn_kernel<KVT, NW>), grid, dim3(64 * NW), 0, st, a);
   return hipGetLastError();
