@@ -102,3 +102,30 @@ def test_fp8_qk_h64_q4_64k(monkeypatch):
 @pytest.mark.slow
 def test_fp8_qk_config3_full_size(monkeypatch):
     _variant(monkeypatch, {}, "config 3 full size L=1048576")
+
+
+@pytest.mark.parametrize("n_kv,H,n_q", [(2, 32, 4), (1, 64, 2), (1, 128, 2)])
+def test_fp8_qk_row_group_counts(monkeypatch, n_kv, H, n_q):
+    """The FP8 product form at each row-group count of the many-row kernel (R = 64, 128, 256 rows per
+    KV head: 2, 4 and 8 waves), two KV heads, lengths ending inside a super-tile: G3 on the full
+    layer and on the sparse layers (oracle on the GPU's own lists)."""
+    banner(f"FP8 Q K^T many-row pass: n_kv={n_kv} H={H} n_q={n_q}")
+    rng = np.random.default_rng(70 + H + n_q + n_kv)
+    lens = [5000, 777]
+    tot = sum(lens)
+    k = rng.standard_normal((tot, n_kv, 128)).astype(np.float32)
+    v = rng.standard_normal((tot, n_kv, 128)).astype(np.float32)
+    q = synth.bf16_bits(rng.standard_normal((2, n_q, H, 128)).astype(np.float32))
+    case = dict(spec=dict(kv="e4m3", q="bf16"), lengths=np.array(lens), row_start=np.array([0, lens[0]]),
+                q_full=q, q_sparse=[q], k=k, v=v, needles=[[], []])
+    up = Uploaded(case)
+    monkeypatch.setenv("HS_MANY_ROW_FP8_QK", "1")
+    res = _run(up, top_k=200, window=16)
+    monkeypatch.delenv("HS_MANY_ROW_FP8_QK")
+    for i in range(2):
+        st = _gates(up, res, i, top_k=200, window=16)
+        print(f"[result] fp8-qk n_kv={n_kv} H={H} n_q={n_q} seq {i}: max|dO| {st['err']:.3e} sparse "
+              f"{st['serr']:.3e} LSE rel {st['lse_rel']:.2e} recall {st['hit'] / st['tot']:.4f}", flush=True)
+        assert st["counts_ok"]
+        assert st["err"] <= TOL_FP8 and st["serr"] <= TOL_FP8
+        assert st["lse_rel"] <= 1e-2
