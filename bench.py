@@ -448,7 +448,7 @@ def bench_append_step(dev, bl, step, flush, use_graph, steps, H, n_q):
 
 def bench_prefill(dev, iters):
     """A 32768-token prompt prefilled in 4 chunks of 8192 (hs_prefill_chunk): per chunk, sliding-window
-    attention (H = 32 on one bf16 KV head, window 128) over the growing Self-Decoder cache, then KV
+    attention (H = 32 on one bf16 KV head, window 128, bf16 output) over the growing Self-Decoder cache, then KV
     Bridging of its hidden states [8192, 4096] into 4 FP8 targets at rows 262144 + 8192 c."""
     import torch
     from long_context_split_amd import hysparse as hs
@@ -468,7 +468,7 @@ def bench_prefill(dev, iters):
                      torch.empty((cap, 1), dtype=torch.float32, device=dev),
                      torch.empty((cap, 1), dtype=torch.float32, device=dev)) for _ in range(nt)]
     caches = [hs.KVCache(k, v, [T * (c + 1)], [0]) for c in range(nch)]
-    outs = [torch.empty((1, T, H, 128), dtype=torch.float32, device=dev) for _ in range(nch)]
+    outs = [torch.empty((1, T, H, 128), dtype=torch.bfloat16, device=dev) for _ in range(nch)]   # bf16 attention output
 
     def prompt():
         for c in range(nch):
@@ -485,8 +485,8 @@ def bench_prefill(dev, iters):
     ms = statistics.median(a.elapsed_time(b) for a, b in evs)
     flops = 2.0 * P * D * nt * 2 * 128 + 4.0 * sum(min(t + 1, w) for t in range(P)) * H * 128
     log(f"prefill {nch} x {T} tokens: {ms * 1e3:.1f} us ({P / (ms * 1e-3):.0f} tokens/s)")
-    return {"workload": f"{P}-token prompt in {nch} chunks of {T}: sliding-window attention (H={H}, w={w}, bf16) "
-                        f"+ KV Bridging [{T}, {D}] -> {nt} FP8 targets per chunk",
+    return {"workload": f"{P}-token prompt in {nch} chunks of {T}: sliding-window attention (H={H}, w={w}, bf16 "
+                        f"cache, bf16 output) + KV Bridging [{T}, {D}] -> {nt} FP8 targets per chunk",
             "ms": round(ms, 4), "tokens_per_s": round(P / (ms * 1e-3), 1), "flops": flops,
             "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
 
@@ -616,26 +616,32 @@ def bench_swa(dev, iters, w=128):
     v = torch.randn((T, 1, 128), generator=g, device=dev).to(torch.bfloat16)
     q = torch.randn((1, T, H, 128), generator=g, device=dev).to(torch.bfloat16)
     kv = hs.KVCache(k, v, [T], [0])
-    out = torch.empty((1, T, H, 128), dtype=torch.float32, device=dev)
-    for _ in range(2):
-        hs.swa_attn(kv, q, w, out=out)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
-    for a, b in evs:
-        a.record()
-        hs.swa_attn(kv, q, w, out=out)
-        b.record()
-    torch.cuda.synchronize()
-    ms = statistics.median(a.elapsed_time(b) for a, b in evs)
-    nbytes = T * H * 128 * 2 + T * H * 128 * 4 + 2 * T * 128 * 2      # Q in, O out, K and V once
     band = sum(min(t + 1, w) for t in range(T))
     flops = 4.0 * band * H * 128                                       # Q K^T and P V over each band
-    gbps = nbytes / (ms * 1e-3) / 1e9
-    log(f"swa: {ms * 1e3:.1f} us  {gbps:.0f} GB/s  ({gbps / HBM_PEAK_GBPS:.3f} of HBM peak)")
+
+    def timed(out):
+        for _ in range(2):
+            hs.swa_attn(kv, q, w, out=out)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        for a, b in evs:
+            a.record()
+            hs.swa_attn(kv, q, w, out=out)
+            b.record()
+        torch.cuda.synchronize()
+        return statistics.median(a.elapsed_time(b) for a, b in evs)
+
+    res = {}
+    for name, dt, ob in (("f32", torch.float32, 4), ("bf16", torch.bfloat16, 2)):
+        ms = timed(torch.empty((1, T, H, 128), dtype=dt, device=dev))
+        nbytes = T * H * 128 * 2 + T * H * 128 * ob + 2 * T * 128 * 2  # Q in, O out, K and V once
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        log(f"swa ({name} output): {ms * 1e3:.1f} us  {gbps:.0f} GB/s  ({gbps / HBM_PEAK_GBPS:.3f} of HBM peak)")
+        res[name] = {"us": round(ms * 1e3, 2), "GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "bytes": nbytes, "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
     return {"workload": f"swa_chunk_32k: 32768-token chunk over its 32768-row bf16 cache, H=32, n_kv=1, window {w}",
-            "us": round(ms * 1e3, 2), "bound": "hbm", "GBps": round(gbps, 1), "peak_GBps": HBM_PEAK_GBPS,
-            "frac": round(gbps / HBM_PEAK_GBPS, 4), "bytes": nbytes, "flops": flops,
-            "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+            "bound": "hbm", "peak_GBps": HBM_PEAK_GBPS, "flops": flops, **res["f32"],
+            "bf16_output": res["bf16"]}
 
 
 def cpu_baseline(case, spec, top_k, window, budget_s):

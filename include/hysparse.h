@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define HS_ABI_VERSION 2
+#define HS_ABI_VERSION 3
 
 typedef enum {
   HS_OK = 0,
@@ -275,11 +275,20 @@ hs_status hs_sparse_attn_noalloc(const hs_kv_cache *kv, const hs_attn_params *p,
 hs_status hs_swa_attn(const hs_kv_cache *kv, const hs_attn_params *p, const void *q,
                       hs_dtype q_dtype, float *out, void *stream);
 
+/* hs_swa_attn with the output type chosen by the caller: out_dtype HS_F32 (the
+ * same call as hs_swa_attn) or HS_BF16, where out holds each float32 result
+ * rounded to bf16 (nearest, ties to even), half the output bytes.  out must be
+ * 16-byte aligned either way.  Errors: as hs_swa_attn, and
+ * HS_ERR_INVALID_ARGUMENT for another out_dtype. */
+hs_status hs_swa_attn_out(const hs_kv_cache *kv, const hs_attn_params *p, const void *q,
+                          hs_dtype q_dtype, void *out, hs_dtype out_dtype, void *stream);
+
 /* One prefill chunk of a prompt on the Self-Decoder side, feeding the
  * Cross-Decoder (ithome page, prefill early-exit paragraphs: prefill runs only
  * the first half of the layers plus the bridging projections, which fill every
  * Cross-Decoder full layer's cache; toolnavs page "Prefill は半分で終わる").
- * Exactly hs_swa_attn(self_kv, swa_p, q, q_dtype, swa_out, stream) followed by
+ * Exactly hs_swa_attn_out(self_kv, swa_p, q, q_dtype, swa_out, swa_out_dtype,
+ * stream) followed by
  * hs_kv_bridge(hidden, n_tokens, d_model, n_targets, w_k, w_v, targets,
  * row_offset, stream) on the same stream: the chunk's n_tokens queries attend
  * to their bands of the Self-Decoder cache (the chunk's rows appended at its
@@ -291,10 +300,10 @@ hs_status hs_swa_attn(const hs_kv_cache *kv, const hs_attn_params *p, const void
  * swa_p->q_tokens must equal n_tokens.  Every check of both steps runs before
  * either is launched; errors as the two calls. */
 hs_status hs_prefill_chunk(const hs_kv_cache *self_kv, const hs_attn_params *swa_p, const void *q,
-                           hs_dtype q_dtype, float *swa_out, const void *hidden, int64_t n_tokens,
-                           int32_t d_model, int32_t n_targets, const void *const *w_k,
-                           const void *const *w_v, const hs_kv_cache *const *targets,
-                           int64_t row_offset, void *stream);
+                           hs_dtype q_dtype, void *swa_out, hs_dtype swa_out_dtype,
+                           const void *hidden, int64_t n_tokens, int32_t d_model, int32_t n_targets,
+                           const void *const *w_k, const void *const *w_v,
+                           const hs_kv_cache *const *targets, int64_t row_offset, void *stream);
 
 /* The selection stage alone, on caller-given float32 scores (a test hook for
  * checking the selection bit for bit).  scores: device float

@@ -438,8 +438,9 @@ hs_status sparse_attn_impl(const hs_kv_cache* kv, const hs_attn_params* p, const
                            size_t workspace_bytes, bool noalloc, void* stream);
 
 // hs_swa_attn's checks and launch arguments (nothing is launched here).
-hs_status swa_prepare(const hs_kv_cache* kv, const hs_attn_params* p, const void* q, hs_dtype q_dtype, float* out,
-                      hs::AttnArgs& a) {
+// od: the output dtype's value, read from the caller's enum as an int (a C caller may pass any value)
+hs_status swa_prepare(const hs_kv_cache* kv, const hs_attn_params* p, const void* q, hs_dtype q_dtype, void* out,
+                      int32_t od, hs::AttnArgs& a) {
   CacheInfo ci;
   hs_status st = check_cache(kv, ci, true);
   if (st != HS_OK) return st;
@@ -456,6 +457,7 @@ hs_status swa_prepare(const hs_kv_cache* kv, const hs_attn_params* p, const void
       return fail(HS_ERR_INVALID_ARGUMENT, "q_tokens %d > seq_len[%d] = %d", p->q_tokens, b, kv->h_seq_len[b]);
   if (!q || !out) return fail(HS_ERR_INVALID_ARGUMENT, "q/out is NULL");
   if (q_dtype != HS_BF16) return fail(HS_ERR_UNSUPPORTED, "q dtype must be BF16");
+  if (od != HS_F32 && od != HS_BF16) return fail(HS_ERR_INVALID_ARGUMENT, "output dtype %d (F32 or BF16)", (int)od);
   if (kv->dtype == HS_F32) return fail(HS_ERR_UNSUPPORTED, "F32 caches are not supported here");
   if (!aligned16(q) || !aligned16(out)) return fail(HS_ERR_INVALID_ARGUMENT, "q/out not 16-byte aligned");
   if ((int64_t)kv->batch * ci.n_kv > MAX_LISTS) return fail(HS_ERR_UNSUPPORTED, "batch * num_kv_heads > 65535");
@@ -466,7 +468,7 @@ hs_status swa_prepare(const hs_kv_cache* kv, const hs_attn_params* p, const void
   a.n_kv = ci.n_kv; a.H = p->num_q_heads; a.G = p->num_q_heads / ci.n_kv; a.n_q = p->q_tokens;
   a.R = a.G; a.n_lists = kv->batch * ci.n_kv;
   a.scale_log2 = scale_log2(p);
-  a.out = out; a.window = p->window;
+  a.out = (float*)out; a.out_bf16 = od == HS_BF16; a.window = p->window;
   return HS_OK;
 }
 
@@ -777,9 +779,16 @@ hs_status hs_sparse_attn_noalloc(const hs_kv_cache* kv, const hs_attn_params* p,
 
 hs_status hs_swa_attn(const hs_kv_cache* kv, const hs_attn_params* p, const void* q, hs_dtype q_dtype,
                       float* out, void* stream) {
+  return hs_swa_attn_out(kv, p, q, q_dtype, out, HS_F32, stream);
+}
+
+hs_status hs_swa_attn_out(const hs_kv_cache* kv, const hs_attn_params* p, const void* q, hs_dtype q_dtype,
+                          void* out, hs_dtype out_dtype, void* stream) {
   g_last_error.clear();
+  int32_t od;
+  memcpy(&od, &out_dtype, sizeof od);
   hs::AttnArgs a{};
-  hs_status st = swa_prepare(kv, p, q, q_dtype, out, a);
+  hs_status st = swa_prepare(kv, p, q, q_dtype, out, od, a);
   if (st != HS_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = timed("swa_attn", s, [&] { return hs::launch_swa_attn(a, kv_type(kv->dtype), s); });
@@ -847,12 +856,14 @@ hs_status hs_kv_bridge(const void* hidden, int64_t n_tokens, int32_t d_model, in
 }
 
 hs_status hs_prefill_chunk(const hs_kv_cache* self_kv, const hs_attn_params* swa_p, const void* q, hs_dtype q_dtype,
-                           float* swa_out, const void* hidden, int64_t n_tokens, int32_t d_model, int32_t n_targets,
-                           const void* const* w_k, const void* const* w_v, const hs_kv_cache* const* targets,
-                           int64_t row_offset, void* stream) {
+                           void* swa_out, hs_dtype swa_out_dtype, const void* hidden, int64_t n_tokens,
+                           int32_t d_model, int32_t n_targets, const void* const* w_k, const void* const* w_v,
+                           const hs_kv_cache* const* targets, int64_t row_offset, void* stream) {
   g_last_error.clear();
+  int32_t od;
+  memcpy(&od, &swa_out_dtype, sizeof od);
   hs::AttnArgs sa;
-  hs_status st = swa_prepare(self_kv, swa_p, q, q_dtype, swa_out, sa);
+  hs_status st = swa_prepare(self_kv, swa_p, q, q_dtype, swa_out, od, sa);
   if (st != HS_OK) return st;
   if (self_kv->batch != 1) return fail(HS_ERR_INVALID_ARGUMENT, "the chunk belongs to one prompt: batch %d", self_kv->batch);
   if (swa_p->q_tokens != n_tokens)

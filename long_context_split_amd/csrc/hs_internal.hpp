@@ -50,6 +50,7 @@ struct AttnArgs {
   uint32_t* zero2_ptr;   // attn_wave: a second run of words cleared by the grid (nullable)
   int64_t zero2_words;
   int qk_fp8;            // attn_rows on an E4M3 cache: Q K^T on FP8 MFMA (Q quantised per row)
+  int out_bf16;          // swa_attn: out holds bf16 (round to nearest even) instead of float
 };
 
 constexpr int CODE_TILE_BYTES = 1152;      // 1024 bytes of codes + 32 float references

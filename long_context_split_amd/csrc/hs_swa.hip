@@ -19,7 +19,7 @@
 // each, the token order of the P operand).
 // Bands overlap between neighbouring workgroups too, so K/V rows come mostly from L2; the kernel's
 // HBM traffic is Q in and O out.  O leaves through a per-wave LDS staging area as whole 128-byte pieces
-// of head rows.
+// of head rows (float32), or as 64-byte pieces rounded to bf16 when the caller asks for bf16 output.
 
 #include "hs_common.hpp"
 #include "hs_internal.hpp"
@@ -210,7 +210,9 @@ __global__ __launch_bounds__(64 * NW, 2) void swa_attn_kernel(AttnArgs a) {
   // tiles are dead after the loop's last barrier) and leave as whole 128-byte pieces of head rows
   float* const ob = (float*)smem + wave * (32 * OPITCH);
   const int nh = min(32, a.G - hb * 32);                          // heads of this block that exist
-  float* const obase = a.out + (((size_t)b * a.n_q + i) * a.H + (size_t)g * a.G + hb * 32) * D;
+  const size_t oel = (((size_t)b * a.n_q + i) * a.H + (size_t)g * a.G + hb * 32) * D;   // first element
+  float* const obase = a.out + oel;
+  uint16_t* const obase16 = (uint16_t*)a.out + oel;
 #pragma unroll
   for (int mt4 = 0; mt4 < 4; ++mt4) {
 #pragma unroll
@@ -221,10 +223,20 @@ __global__ __launch_bounds__(64 * NW, 2) void swa_attn_kernel(AttnArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (a.out_bf16) {                                             // head 16 k + lane / 4, d octet lane % 4
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {                                 // head 8 k + lane / 8, d quad lane % 8
-      const int hd = 8 * k + (lane >> 3), pc = lane & 7;
-      if (hd < nh) *(f32x4*)(obase + (size_t)hd * D + 32 * mt4 + 4 * pc) = *(const f32x4*)(ob + hd * OPITCH + 4 * pc);
+      for (int k = 0; k < 2; ++k) {
+        const int hd = 16 * k + (lane >> 2), pc = lane & 3;
+        const f32x4 x0 = *(const f32x4*)(ob + hd * OPITCH + 8 * pc), x1 = *(const f32x4*)(ob + hd * OPITCH + 8 * pc + 4);
+        const u32x4 w = {pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]), pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3])};
+        if (hd < nh) *(u32x4*)(obase16 + (size_t)hd * D + 32 * mt4 + 8 * pc) = w;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {                               // head 8 k + lane / 8, d quad lane % 8
+        const int hd = 8 * k + (lane >> 3), pc = lane & 7;
+        if (hd < nh) *(f32x4*)(obase + (size_t)hd * D + 32 * mt4 + 4 * pc) = *(const f32x4*)(ob + hd * OPITCH + 4 * pc);
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");        // reads done before the next block's writes
     __builtin_amdgcn_wave_barrier();

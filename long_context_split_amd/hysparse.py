@@ -17,7 +17,7 @@ LIB_PATH = os.environ.get("HYSPARSE_LIB") or os.path.join(_HERE, "libhysparse.so
 
 HS_OK, HS_ERR_INVALID_ARGUMENT, HS_ERR_UNSUPPORTED, HS_ERR_WORKSPACE_TOO_SMALL, HS_ERR_HIP = range(5)
 HS_F32, HS_BF16, HS_FP8_E4M3 = 0, 1, 2
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class HsError(RuntimeError):
@@ -87,9 +87,12 @@ lib.hs_sparse_attn_noalloc.restype = ctypes.c_int
 lib.hs_sparse_attn_noalloc.argtypes = [_KVP, _PP, _P, ctypes.c_int, _P, _P, _P, _P]
 lib.hs_swa_attn.restype = ctypes.c_int
 lib.hs_swa_attn.argtypes = [_KVP, _PP, _P, ctypes.c_int, _P, _P]
+lib.hs_swa_attn_out.restype = ctypes.c_int
+lib.hs_swa_attn_out.argtypes = [_KVP, _PP, _P, ctypes.c_int, _P, ctypes.c_int, _P]
 lib.hs_prefill_chunk.restype = ctypes.c_int
-lib.hs_prefill_chunk.argtypes = [_KVP, _PP, _P, ctypes.c_int, _P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
-                                 ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_KVP), ctypes.c_int64, _P]
+lib.hs_prefill_chunk.argtypes = [_KVP, _PP, _P, ctypes.c_int, _P, ctypes.c_int, _P, ctypes.c_int64, ctypes.c_int32,
+                                 ctypes.c_int32, ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_KVP),
+                                 ctypes.c_int64, _P]
 lib.hs_select_from_scores.restype = ctypes.c_int
 lib.hs_select_from_scores.argtypes = [_P, _P, ctypes.POINTER(ctypes.c_int32)] + [ctypes.c_int32] * 7 + \
     [_P, _P, _P, ctypes.c_size_t, _P]
@@ -284,14 +287,24 @@ def sparse_attn_noalloc(kv, q, sel_idx, sel_count, top_k=1024, window=128, softm
     return out
 
 
-def swa_attn(kv, q, window, softmax_scale=0.0, out=None, stream=None):
+def _out_dtype(t):
+    if t.dtype == torch.float32:
+        return HS_F32
+    if t.dtype == torch.bfloat16:
+        return HS_BF16
+    raise TypeError(f"unsupported output tensor dtype {t.dtype}")
+
+
+def swa_attn(kv, q, window, softmax_scale=0.0, out=None, out_dtype=torch.float32, stream=None):
     """Sliding-window attention of the last q_tokens cache rows of every sequence (band of `window`
-    rows ending at each query's own row).  Returns out [B, n_q, H, 128] float32."""
+    rows ending at each query's own row).  Returns out [B, n_q, H, 128], float32 or bf16 (the dtype of
+    a given `out`, else `out_dtype`)."""
     B, n_q, H, d = q.shape
     p = params(H, n_q, 0, window, softmax_scale)
     if out is None:
-        out = torch.empty((B, n_q, H, d), dtype=torch.float32, device=q.device)
-    check(lib.hs_swa_attn(kv.c, ctypes.byref(p), _ptr(q), query_dtype(q), _ptr(out), _stream(stream)))
+        out = torch.empty((B, n_q, H, d), dtype=out_dtype, device=q.device)
+    check(lib.hs_swa_attn_out(kv.c, ctypes.byref(p), _ptr(q), query_dtype(q), _ptr(out), _out_dtype(out),
+                              _stream(stream)))
     return out
 
 
@@ -323,19 +336,20 @@ def kv_bridge(hidden, w_k, w_v, targets, row_offset, stream=None):
 
 
 def prefill_chunk(self_kv, q, window, hidden, w_k, w_v, targets, row_offset, swa_out=None, softmax_scale=0.0,
-                  stream=None):
+                  swa_out_dtype=torch.float32, stream=None):
     """One Self-Decoder prefill chunk: sliding-window attention of the chunk's queries q [1, T, H, 128]
     (the chunk's rows are the last T rows of self_kv) and KV Bridging of its hidden states [T, Dm] into
     every target at rows [row_offset, row_offset + T).  Returns the attention output [1, T, H, 128]."""
     B, T, H, d = q.shape
     p = params(H, T, 0, window, softmax_scale)
     if swa_out is None:
-        swa_out = torch.empty((B, T, H, d), dtype=torch.float32, device=q.device)
+        swa_out = torch.empty((B, T, H, d), dtype=swa_out_dtype, device=q.device)
     n = len(targets)
     wk = (ctypes.c_void_p * n)(*[w.data_ptr() for w in w_k])
     wv = (ctypes.c_void_p * n)(*[w.data_ptr() for w in w_v])
     tg = (_KVP * n)(*[ctypes.pointer(t._c) for t in targets])
-    check(lib.hs_prefill_chunk(self_kv.c, ctypes.byref(p), _ptr(q), query_dtype(q), _ptr(swa_out), _ptr(hidden),
+    check(lib.hs_prefill_chunk(self_kv.c, ctypes.byref(p), _ptr(q), query_dtype(q), _ptr(swa_out), _out_dtype(swa_out),
+                               _ptr(hidden),
                                hidden.shape[0], hidden.shape[1], n, wk, wv, tg, int(row_offset), _stream(stream)))
     return swa_out
 

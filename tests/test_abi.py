@@ -47,7 +47,7 @@ def test_exports_every_declared_symbol(hs):
 
 
 def test_version_and_strings(hs):
-    assert hs.lib.hs_abi_version() == 2
+    assert hs.lib.hs_abi_version() == 3
     assert hs.status_string(0) == "HS_OK"
     assert hs.status_string(3) == "HS_ERR_WORKSPACE_TOO_SMALL"
 
@@ -252,10 +252,25 @@ def test_prefill_chunk_rejects_before_launch(hs):
     one = _cache(hs, lens=(300,), cap=1000)
     two = _cache(hs, lens=(300, 200), cap=1000)
     p = hs.params(32, 100, 0, 128)
-    args = lambda kv, prm, n, off: (ctypes.byref(kv), ctypes.byref(prm), 0x200000, 1, 0x400000, 0x900000, n, 512,
-                                    1, w, w, tp, off, None)
+    args = lambda kv, prm, n, off, od=0: (ctypes.byref(kv), ctypes.byref(prm), 0x200000, 1, 0x400000, od, 0x900000,
+                                          n, 512, 1, w, w, tp, off, None)
+    assert f(*args(one, p, 100, 0, od=2)) == 1                      # output dtype neither F32 nor BF16
     assert f(*args(two, p, 100, 0)) == 1                            # two sequences
     assert f(*args(one, p, 99, 0)) == 1                             # q_tokens != n_tokens
     assert f(*args(one, p, 100, 950)) == 1                          # bridge rows past the target capacity
     assert f(*args(one, hs.params(32, 100, 0, 0), 100, 0)) == 1     # window < 1
     assert f(*args(one, hs.params(32, 400, 0, 128), 400, 0)) == 1   # more queries than cache rows
+
+
+def test_swa_attn_out_rejects_before_launch(hs):
+    """The sliding-window call with a chosen output type validates that type and everything else
+    hs_swa_attn validates, before touching a device."""
+    f = hs.lib.hs_swa_attn_out
+    c = _cache(hs, lens=(300,), cap=1000)
+    p = hs.params(32, 100, 0, 128)
+    assert f(ctypes.byref(c), ctypes.byref(p), 0x200000, 1, 0x400000, 2, None) == 1          # E4M3 output
+    assert f(ctypes.byref(c), ctypes.byref(p), 0x200000, 1, 0x400000, 7, None) == 1          # unknown dtype
+    assert "output dtype" in hs.last_error()
+    assert f(ctypes.byref(c), ctypes.byref(p), 0x200000, 1, 0x400008, 1, None) == 1          # misaligned out
+    assert f(ctypes.byref(c), ctypes.byref(p), 0x200000, 1, None, 1, None) == 1              # NULL out
+    assert f(ctypes.byref(c), ctypes.byref(hs.params(32, 100, 0, 0)), 0x200000, 1, 0x400000, 1, None) == 1

@@ -18,10 +18,13 @@ from test_gpu_bridge import SENT8, SENTF, _targets, _host, _check_random, _untou
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("fp8,chunks,w", [(True, [700, 700, 613], 256), (False, [512, 1024, 300, 77], 600)])
-def test_prefill_chunks_feed_bridge_targets(fp8, chunks, w):
+@pytest.mark.parametrize("fp8,chunks,w,out16", [(True, [700, 700, 613], 256, True),
+                                                (False, [512, 1024, 300, 77], 600, False)])
+def test_prefill_chunks_feed_bridge_targets(fp8, chunks, w, out16):
+    """out16: the attention output in bf16, checked within the float32 bound plus half a bf16 step."""
+    from oracle import bf16
     from long_context_split_amd import hysparse as hs
-    banner(f"prefill chunks={chunks} w={w} fp8 targets={fp8}")
+    banner(f"prefill chunks={chunks} w={w} fp8 targets={fp8} bf16 attention output={out16}")
     P, H, D, nt, base = sum(chunks), 32, 512, 4, 1000
     rng = np.random.default_rng(60 + len(chunks))
     k = synth.bf16_bits(rng.standard_normal((P, 1, 128)).astype(np.float32))
@@ -40,7 +43,7 @@ def test_prefill_chunks_feed_bridge_targets(fp8, chunks, w):
         end = start + T
         self_kv = hs.KVCache(kd, vd, [end], [0])                       # the cache grown by this chunk
         qc = dev_bf16(q[start:end]).reshape(1, T, H, 128)
-        o = torch.full((1, T, H, 128), float("nan"), dtype=torch.float32, device="cuda")
+        o = torch.full((1, T, H, 128), float("nan"), dtype=torch.bfloat16 if out16 else torch.float32, device="cuda")
         hs.prefill_chunk(self_kv, qc, w, x[start:end], wk, wv, tg, base + start, swa_out=o)
         outs.append(o)
         start = end
@@ -52,7 +55,11 @@ def test_prefill_chunks_feed_bridge_targets(fp8, chunks, w):
     for T, o in zip(chunks, outs):
         end = start + T
         ref = swa.swa_attention(block.cache_values(q[start:end], "bf16"), kf[:end], vf[:end], w)
-        err = float(np.abs(o[0].cpu().numpy() - ref).max())
+        if out16:
+            got = bf16.decode(o[0].view(torch.int16).cpu().numpy().view(np.uint16))
+            err = float(np.max(np.abs(got - ref) - np.ldexp(1.0, np.frexp(np.abs(ref) + 2e-3)[1] - 9)))
+        else:
+            err = float(np.abs(o[0].cpu().numpy() - ref).max())
         worst = max(worst, err)
         assert err <= 2e-3, f"chunk at {start}: max-abs {err}"
         start = end

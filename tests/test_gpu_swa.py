@@ -57,6 +57,41 @@ def test_swa_parity(kvtype, lens, n_kv, H, n_q, w):
     print(f"[result] swa {kvtype} w={w} max-abs {worst:.2e}", flush=True)
 
 
+@pytest.mark.parametrize("kvtype,lens,n_kv,H,n_q,w", [
+    ("bf16", [517, 250], 1, 32, 200, 100),
+    ("e4m3", [400], 2, 64, 37, 33),
+    ("bf16", [260], 1, 40, 21, 64),
+])
+def test_swa_bf16_output(kvtype, lens, n_kv, H, n_q, w):
+    """bf16 output (hs_swa_attn_out): bit for bit the float32 call's results rounded to nearest even
+    (the oracle's bf16 encoder applied to them), every element written, and within the float32
+    tolerance plus half a bf16 step of the float64 oracle."""
+    from oracle import bf16
+    from long_context_split_amd import hysparse as hs
+    banner(f"swa bf16 output {kvtype} lens={lens} n_kv={n_kv} H={H} n_q={n_q} w={w}")
+    up = _case(kvtype, lens, n_kv, H, n_q, seed=len(lens) * 1000 + w + H)
+    B, nq, Hq, _ = up.q_full.shape
+    f32 = hs.swa_attn(up.kv, up.q_full, w)
+    poison = torch.full((B, nq, Hq, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    o16 = hs.swa_attn(up.kv, up.q_full, w, out=poison)
+    torch.cuda.synchronize()
+    bits = o16.view(torch.int16).cpu().numpy().view(np.uint16)
+    f32 = f32.cpu().numpy()
+    assert np.array_equal(bits, bf16.encode_rne(f32.astype(np.float64)))
+    got = bf16.decode(bits)
+    tol = 2e-3 if kvtype == "bf16" else 3e-2
+    worst = 0.0
+    for i in range(len(lens)):
+        q, k, v = up.oracle_seq(i)
+        ref = swa.swa_attention(q, k, v, w)
+        half_step = np.ldexp(1.0, np.frexp(np.abs(ref) + tol)[1] - 9)      # half a bf16 step of |ref| + tol
+        excess = float(np.max(np.abs(got[i] - ref) - half_step))
+        worst = max(worst, excess)
+        assert excess <= tol, f"sequence {i}: max excess over half a bf16 step {excess}"
+    print(f"[result] swa bf16-out {kvtype} w={w}: equal to the float32 call rounded; "
+          f"max-abs error beyond half a bf16 step {worst:.2e}", flush=True)
+
+
 def test_swa_rejects_bad_arguments():
     from long_context_split_amd import hysparse as hs
     up = _case("bf16", [50], 1, 32, 10, seed=7)
