@@ -84,9 +84,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); the hybrid-block "
-              "path has no multi-GPU mode in this build (independent sequences would shard as pure data "
-              "parallelism with no exchange)", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); the library has no "
+              "multi-GPU mode (independent sequences would shard as pure data parallelism with no exchange)",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

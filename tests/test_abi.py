@@ -244,7 +244,7 @@ def test_sparse_attn_noalloc_rejects_before_launch(hs):
 
 
 def test_prefill_chunk_rejects_before_launch(hs):
-    """The chunk driver checks both of its steps (and that they describe the same chunk) first."""
+    """The chunk call checks both of its steps (and that they describe the same chunk) first."""
     f = hs.lib.hs_prefill_chunk
     tgt = _cache(hs, dtype=2, scales=True, lens=(1,), cap=1000)
     tp = (ctypes.POINTER(hs.hs_kv_cache) * 1)(ctypes.pointer(tgt))
