@@ -86,13 +86,18 @@ def _check_seq(up, res, i, top_k=1024, window=128, check_sparse=True, stats=None
     if check_sparse:
         gidx = res["idx"][i]
         gcnt = res["cnt"][i]
+        same = np.array_equal(gidx, ref["idx"]) and np.array_equal(gcnt, ref["cnt"])
         for layer in range(len(up.q_sparse)):
             qs, _, _ = up.oracle_seq(i, "sparse", layer)
             so, _ = attention.sparse_attention(qs, k, v, gidx, gcnt)
             e = np.abs(res["sparse"][layer][i] - so).max()
             assert e <= tol, f"seq {i} sparse layer {layer}: max|dO| = {e}"
+            # second report (not a gate): against the oracle run on its own lists, where boundary
+            # swaps between near-tied scores would show up
+            eo = e if same else np.abs(res["sparse"][layer][i] - attention.sparse_attention(qs, k, v, ref["idx"], ref["cnt"])[0]).max()
             if stats is not None:
                 stats["serr"] = max(stats.get("serr", 0.0), float(e))
+                stats["serr_own"] = max(stats.get("serr_own", 0.0), float(eo))
     return hit, tot
 
 
@@ -112,9 +117,10 @@ def _same_lists_without_scores(up, res, top_k=1024, window=128):
 
 
 def _recall_report(stats):
-    """Plain recall, tie-aware recall and the worst single list (gate G2 uses the plain one)."""
+    """Plain recall, tie-aware recall and the worst single list (gate G2 uses the plain one), and the
+    sparse layers' largest error against the oracle on its own lists (a report, not a gate)."""
     return (f"recall {stats['hit'] / stats['tot']:.6f} tie-aware {stats['tie'] / stats['tot']:.6f} "
-            f"worst list {stats['worst']:.6f}")
+            f"worst list {stats['worst']:.6f}; sparse vs the oracle's own lists {stats.get('serr_own', 0.0):.3e}")
 
 
 def test_config1_fp32_full_size():

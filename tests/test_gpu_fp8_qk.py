@@ -8,7 +8,8 @@ The selection scores still come from the bf16 score pass; what the FP8 products 
 full layer's O and LSE (Q rounded to E4M3 per query row), and through the LSE each head's weight
 in the scores.  Measured on MI355X: G3 holds with a wide margin (max |dO| about 8e-4), but the LSE
 moves by about 1e-3 relative and recall falls to 0.997 at 64K and 0.991 at 1M rows (tie-aware
-recall the same: the swapped rows are not near-ties), below G2.  The variant is therefore not
+recall the same: the swapped rows are not near-ties), below G2, and the sparse layers on the moved
+lists differ from the exact method's (the oracle on its own lists) by up to 6e-2 to 8e-2.  The variant is therefore not
 adopted: the switch (HS_MANY_ROW_FP8_QK=1) stays off by default.  These tests hold G3 and the
 list shapes, require recall >= 0.98 (a broken product would drop it far lower) and print the
 measured G2 figures.
@@ -66,10 +67,14 @@ def _gates(up, res, i=0, top_k=1024, window=128):
             st["tie"] += th
             if n:
                 st["worst"] = min(st["worst"], h / n)
+    st["serr_own"] = 0.0
     for layer in range(len(up.q_sparse)):
         qs, _, _ = up.oracle_seq(i, "sparse", layer)
         so, _ = attention.sparse_attention(qs, k, v, res["idx"][i], res["cnt"][i])
         st["serr"] = max(st["serr"], float(np.abs(res["sparse"][layer][i] - so).max()))
+        # second report: the oracle on its own lists (the rows the rounded Q moved across the boundary)
+        so_own, _ = attention.sparse_attention(qs, k, v, ref["idx"], ref["cnt"])
+        st["serr_own"] = max(st["serr_own"], float(np.abs(res["sparse"][layer][i] - so_own).max()))
     return st
 
 
@@ -86,7 +91,8 @@ def _variant(monkeypatch, cfg_kwargs, label):
     print(f"[result] fp8-qk {label}: G3 full max|dO| {st['err']:.3e} sparse {st['serr']:.3e} "
           f"(vs the bf16 form: max|dO| {d_bf16:.3e}, list entries equal {same_lists:.6f}); "
           f"LSE rel {st['lse_rel']:.2e}; G2 recall {st['hit'] / st['tot']:.6f} "
-          f"tie-aware {st['tie'] / st['tot']:.6f} worst list {st['worst']:.6f}", flush=True)
+          f"tie-aware {st['tie'] / st['tot']:.6f} worst list {st['worst']:.6f}; sparse vs the oracle's own "
+          f"lists {st['serr_own']:.3e}", flush=True)
     assert st["counts_ok"]
     assert st["err"] <= TOL_FP8 and st["serr"] <= TOL_FP8             # G3
     assert st["hit"] / st["tot"] >= 0.98                              # below G2's 0.999: not adopted
