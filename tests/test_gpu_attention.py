@@ -310,6 +310,17 @@ def test_many_row_kernels(kvtype, n_kv, H, n_q):
         _check_seq(up, res, i, top_k=200, window=16)
 
 
+@pytest.mark.parametrize("top_k,window", [(0, 32), (50, 0)])
+def test_degenerate_budgets(top_k, window):
+    """The full layer and the sparse layers with no global budget (the window alone) and with no
+    window (the global tokens alone), bf16 and a length shorter than the window."""
+    banner(f"degenerate budgets top_k={top_k} window={window}")
+    up = Uploaded(synth.decode_case(2, B=3, lengths=[300, 20, 2000]))
+    res = _run_block(up, top_k=top_k, window=window)
+    for i in range(3):
+        _check_seq(up, res, i, top_k=top_k, window=window)
+
+
 def test_fp8_cache_h64_q4():
     """Config 3's shape (H=64, 4 query tokens, FP8 E4M3 with per-token scales,
     near-duplicate key clusters) at a 64K context."""

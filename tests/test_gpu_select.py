@@ -75,6 +75,17 @@ def test_select_many_queries_and_kv_heads():
     _check(full, lens, 3, 2, 100, 0)
 
 
+def test_select_zero_budgets():
+    """Degenerate budgets: no global tokens (top_k 0: the window alone) and no window (the global
+    tokens alone)."""
+    banner("select top_k=0 / window=0")
+    rng = np.random.default_rng(13)
+    lens = [1, 100, 129, 3000]
+    full = rng.random((4, 2, 1, max(lens))).astype(np.float32)
+    _check(np.ascontiguousarray(full[..., :max(lens) - 128]), lens, 2, 1, 0, 128)
+    _check(full, lens, 2, 1, 50, 0)
+
+
 def test_select_one_million_candidates():
     banner("select L=1048576")
     rng = np.random.default_rng(9)
