@@ -427,6 +427,16 @@ def test_block_level_variant_bf16():
         assert cnt[i, 0, 0] == gc and np.array_equal(idx[i, 0, 0], gi), f"seq {i}: block lists"
         oi, oc = selection.select_blocks(ref["s"][0, 0], L, 1024, 128)
         assert gc == oc
+        # order-free check on the same float32 scores: with float64 block sums, no unchosen block
+        # beats a chosen one by more than the float32 pairwise tree can move two sums (six levels
+        # of rounding on non-negative terms: at most 6 u (1 + u)^6 relative each, u = 2^-24)
+        n = L - w
+        bs64 = selection.block_scores(sc[i, 0, 0, :n].astype(np.float64))
+        chosen = np.zeros(bs64.shape[0], dtype=bool)
+        chosen[np.unique(gi[:gc - w] // 64)] = True
+        if 0 < chosen.sum() < chosen.size:
+            eps = 7.0 * 2.0 ** -24
+            assert bs64[chosen].min() * (1 + eps) >= bs64[~chosen].max() * (1 - eps), f"seq {i}: block dominance"
         g = set(gi[:gc - w].tolist())
         r = set(oi[:oc - w].tolist())
         hit += len(g & r)
