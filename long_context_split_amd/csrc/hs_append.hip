@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void append_finish_kernel(AppendArgs a) {
   }
   const int64_t row = a.rows[tok];
   if (a.fp8) {
-    const float am = wave_max(fmaxf(fabsf(v.x), fabsf(v.y)));
+    const float am = wave_max_dpp(fmaxf(fabsf(v.x), fabsf(v.y)));
     float scale = am / 448.0f;                                     // correctly rounded
     if (scale == 0.f) scale = 1.f;
     const uint32_t c0 = f32_to_e4m3_rne(v.x / scale), c1 = f32_to_e4m3_rne(v.y / scale);

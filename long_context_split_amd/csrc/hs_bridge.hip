@@ -185,8 +185,7 @@ __global__ __launch_bounds__(NT) void bridge_kernel(BridgeArgs a) {
         float am = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) am = fmaxf(am, fabsf(acc[i][j][r]));
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) am = fmaxf(am, __shfl_xor(am, o));
+        am = half_max_dpp(am);                                         // the row's 32 lanes
         float scale = am / 448.0f;                                   // correctly rounded
         if (scale == 0.f) scale = 1.f;
         float y[4];

@@ -113,6 +113,44 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Combining v with the value of lane l ^ 32 (or l ^ 16) through v_permlane32_swap_b32
+// (v_permlane16_swap_b32), vector-unit operations, instead of an LDS permute on the latency chain.
+// With v in both operands the swap leaves v of lanes l and l ^ 32 (l ^ 16) in its two results, in
+// an order that depends on the half, so only commutative combinations are formed: the sum equals
+// v + __shfl_xor(v, 32) bit for bit.
+__device__ __forceinline__ float xor32_add(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Maximum over each half of the wave (lanes 0-31, 32-63) without LDS: lane pairs, quads, half rows
+// and rows of 16 by DPP, then the two rows of the half by the 16-lane swap.  Every lane gets the
+// maximum of its half.
+__device__ __forceinline__ float half_max_dpp(float v) {
+  auto dpp = [](float x, int ctl) -> float {
+    switch (ctl) {                                                // the control must be a constant
+      case 0: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));   // l ^ 1
+      case 1: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));   // l ^ 2
+      case 2: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));  // half-row mirror
+      default: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false)); // row mirror
+    }
+  };
+#pragma unroll
+  for (int c = 0; c < 4; ++c) v = fmaxf(v, dpp(v, c));
+  return xor16_max(v);
+}
+
+// Maximum over the wave without LDS (every lane gets it).
+__device__ __forceinline__ float wave_max_dpp(float v) { return xor32_max(half_max_dpp(v)); }
+
 // Selection scores of the 32-token S tile a wave holds (S = Q K^T from v_mfma_f32_32x32x16_bf16:
 // lane l has token l & 31 and the rows 8 (r / 4) + 4 (l >> 5) + (r & 3)): for each of the NQ query
 // tokens of the 32 rows (tpw tokens of G = 32 / tpw rows each, or one token when tpw = 1), the sum
@@ -129,13 +167,13 @@ __device__ __forceinline__ void tile_scores(const f32x16& s, float f, const floa
     float v = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) v += p[r];
-    tv[0] = v + __shfl_xor(v, 32);
+    tv[0] = xor32_add(v);
   } else {
     float blk[4];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       blk[q4] = p[4 * q4] + p[4 * q4 + 1] + p[4 * q4 + 2] + p[4 * q4 + 3];
-      blk[q4] += __shfl_xor(blk[q4], 32);
+      blk[q4] = xor32_add(blk[q4]);
     }
 #pragma unroll
     for (int t = 0; t < NQ; ++t) tv[t] = tpw == 4 ? blk[t] : blk[2 * t] + blk[2 * t + 1];

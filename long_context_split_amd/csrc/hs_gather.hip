@@ -213,7 +213,7 @@ __global__ __launch_bounds__(64 * NW) void attn_gather_kernel(AttnArgs a) {
     float mt = x[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mt = fmaxf(mt, x[r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = xor32_max(mt);
     const float mn = fmaxf(m, mt);
     const float msub = mn == -INFINITY ? 0.f : mn;
     const float alpha = exp2f(m - msub);            // m = -inf: 0
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(64 * NW) void attn_gather_kernel(AttnArgs a) {
     }
     wave_sync();                                    // reads done before the next tile's writes
   }
-  lsum += __shfl_xor(lsum, 32);
+  lsum = xor32_add(lsum);
 
   // ---- combine the NW waves (fixed order) through LDS
   __syncthreads();

@@ -212,7 +212,7 @@ __global__ __launch_bounds__(64 * NRG) void attn_rows_kernel(AttnArgs a) {
       const float f = sk * sl2;
       ksc[tid] = f;
       vsc[tid] = sv;
-      const float fx = wave_max(f), fn = -wave_max(-f);           // the super-tile's extreme factors
+      const float fx = wave_max_dpp(f), fn = -wave_max_dpp(-f);   // the super-tile's extreme factors
       if (lane == 0) { fmm[wave][0] = fx; fmm[wave][1] = fn; }
     }
     __syncthreads();
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(64 * NRG) void attn_rows_kernel(AttnArgs a) {
       float smax = s[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) smax = fmaxf(smax, s[r]);
-      smax = fmaxf(smax, __shfl_xor(smax, 32));
+      smax = xor32_max(smax);
       const float mt = smax * (smax >= 0.f ? fmax_t : fmin_t) * qs; // >= the tile's max logit (log2 units)
       const bool need = mt > m + TAU;                               // same for both lanes of a row
       if (__ballot(need)) {
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(64 * NRG) void attn_rows_kernel(AttnArgs a) {
   }
 
   // ---- one partial per row: acc (unnormalised, d-major in the C layout) and (m, l)
-  lsum += __shfl_xor(lsum, 32);
+  lsum = xor32_add(lsum);
   if (row_ok) {
     const size_t item = (size_t)list * a.max_chunks + chunk;
     float* pa = a.part_acc + (item * a.R + row) * D;
@@ -458,7 +458,7 @@ __global__ __launch_bounds__(64 * NRG) void attn_rows_scores_kernel(ScoreArgs a)
         float v = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) v += exp2_fast(s[4 * q4 + i] * f - lse2[4 * q4 + i]);
-        blk[q4] = v + __shfl_xor(v, 32);
+        blk[q4] = xor32_add(v);
       }
       if (lane < 32) {
         if (tpw == 1) part[wave][0][tk] = (blk[0] + blk[1]) + (blk[2] + blk[3]);

@@ -153,7 +153,7 @@ __global__ __launch_bounds__(64 * NW, 2) void swa_attn_kernel(AttnArgs a) {
       float mt = x[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mt = fmaxf(mt, x[r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      mt = xor32_max(mt);
       const float mn = fmaxf(m, mt);
       const float msub = mn == -INFINITY ? 0.f : mn;
       const float alpha = exp2f(m - msub);
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(64 * NW, 2) void swa_attn_kernel(AttnArgs a) {
     __syncthreads();
   }
   if (!active) return;
-  lsum += __shfl_xor(lsum, 32);
+  lsum = xor32_add(lsum);
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   // ---- output: for each block of 32 d, the wave's 32 heads x 32 d go through its own LDS area (the
   // tiles are dead after the loop's last barrier) and leave as whole 128-byte pieces of head rows
