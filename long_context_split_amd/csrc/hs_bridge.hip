@@ -20,7 +20,7 @@
 // Tile order: the workgroups of one token tile (all targets) are adjacent in dispatch order and land
 // on one XCD, so they share that tile's X rows through the XCD's L2.
 
-// Epilogue in registers: the row amax by lane shuffles, x / scale correctly rounded, E4M3 by the
+// Epilogue in registers: the row amax by DPP and a lane swap, x / scale correctly rounded, E4M3 by the
 // hardware packed conversion (equal to the software RNE conversion for
 // every finite |y| < 448 that does not round to zero, the range used here; a zero magnitude is stored
 // as +0), then a byte (or bf16) transpose inside each quad of lanes so that every store writes whole
