@@ -19,7 +19,8 @@
 // each, the token order of the P operand).
 // Bands overlap between neighbouring workgroups too, so K/V rows come mostly from L2; the kernel's
 // HBM traffic is Q in and O out.  O leaves through a per-wave LDS staging area as whole 128-byte pieces
-// of head rows (float32), or as 64-byte pieces rounded to bf16 when the caller asks for bf16 output.
+// of head rows (float32, 32 d per row and round; bf16, 64 d per row and round, when the caller asks for
+// a bf16 output).
 
 #include "hs_common.hpp"
 #include "hs_internal.hpp"
@@ -33,6 +34,7 @@ constexpr int SKROW = 272;                         // K tile row: 256 B + 16 B p
 constexpr int SVROW = 288;                         // V tile row: 256 B + 32 B pad (4-row transpose reads)
 constexpr int SBUF = 32 * SKROW + 32 * SVROW;      // one tile: K then V (bf16)
 constexpr int OPITCH = 36;                         // output staging: floats per head row (32 d + 4 pad)
+constexpr int OPITCH2 = 68;                        // bf16 output staging: 64 d + 4 pad
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -54,7 +56,8 @@ __global__ __launch_bounds__(64 * NW, 2) void swa_attn_kernel(AttnArgs a) {
   constexpr int PPR = SB / 16;                      // 16-byte pieces per row
   constexpr int PPT = 2 * 32 * PPR / NT;            // 16-byte pieces per thread per tile (K and V)
   static_assert(PPT >= 1 && PPT * NT == 2 * 32 * PPR, "a tile's K and V pieces split evenly over the threads");
-  constexpr int SMEM = 2 * SBUF > NW * 32 * OPITCH * 4 ? 2 * SBUF : NW * 32 * OPITCH * 4;
+  constexpr int STAGE = NW * 32 * OPITCH2 * 4;               // output staging (OPITCH2 > OPITCH)
+  constexpr int SMEM = 2 * SBUF > STAGE ? 2 * SBUF : STAGE;
   __shared__ __align__(16) char smem[SMEM];
   __shared__ float scl[2][2][32];                   // per buffer: K scale x softmax scale, V scale (E4M3)
 
@@ -206,13 +209,43 @@ __global__ __launch_bounds__(64 * NW, 2) void swa_attn_kernel(AttnArgs a) {
   if (!active) return;
   lsum = xor32_add(lsum);
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  // ---- output: for each block of 32 d, the wave's 32 heads x 32 d go through its own LDS area (the
-  // tiles are dead after the loop's last barrier) and leave as whole 128-byte pieces of head rows
-  float* const ob = (float*)smem + wave * (32 * OPITCH);
+  // ---- output: the wave's 32 heads go through its own LDS area (the tiles are dead after the loop's
+  // last barrier) and leave as whole 128-byte pieces of head rows: 32 d per round as float32, 64 d
+  // (two accumulator blocks) per round as bf16
   const int nh = min(32, a.G - hb * 32);                          // heads of this block that exist
   const size_t oel = (((size_t)b * a.n_q + i) * a.H + (size_t)g * a.G + hb * 32) * D;   // first element
+  auto wave_fence = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  if (a.out_bf16) {
+    float* const ob = (float*)smem + wave * (32 * OPITCH2);
+    uint16_t* const obase16 = (uint16_t*)a.out + oel;
+#pragma unroll
+    for (int mp = 0; mp < 2; ++mp) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x16& c = acc[2 * mp + hf];
+          const f32x4 o = {c[4 * r4], c[4 * r4 + 1], c[4 * r4 + 2], c[4 * r4 + 3]};
+          *(f32x4*)(ob + tok * OPITCH2 + 32 * hf + crow(lane, 4 * r4)) = o * inv;
+        }
+      wave_fence();
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {                               // head 8 k + lane / 8, d octet lane % 8
+        const int hd = 8 * k + (lane >> 3), pc = lane & 7;
+        const f32x4 x0 = *(const f32x4*)(ob + hd * OPITCH2 + 8 * pc), x1 = *(const f32x4*)(ob + hd * OPITCH2 + 8 * pc + 4);
+        const u32x4 w = {pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]), pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3])};
+        if (hd < nh) *(u32x4*)(obase16 + (size_t)hd * D + 64 * mp + 8 * pc) = w;
+      }
+      wave_fence();                                               // reads done before the next round's writes
+    }
+    return;
+  }
+  float* const ob = (float*)smem + wave * (32 * OPITCH);
   float* const obase = a.out + oel;
-  uint16_t* const obase16 = (uint16_t*)a.out + oel;
 #pragma unroll
   for (int mt4 = 0; mt4 < 4; ++mt4) {
 #pragma unroll
@@ -220,27 +253,13 @@ __global__ __launch_bounds__(64 * NW, 2) void swa_attn_kernel(AttnArgs a) {
       const f32x4 o = {acc[mt4][4 * r4], acc[mt4][4 * r4 + 1], acc[mt4][4 * r4 + 2], acc[mt4][4 * r4 + 3]};
       *(f32x4*)(ob + tok * OPITCH + crow(lane, 4 * r4)) = o * inv;
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (a.out_bf16) {                                             // head 16 k + lane / 4, d octet lane % 4
+    wave_fence();
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int hd = 16 * k + (lane >> 2), pc = lane & 3;
-        const f32x4 x0 = *(const f32x4*)(ob + hd * OPITCH + 8 * pc), x1 = *(const f32x4*)(ob + hd * OPITCH + 8 * pc + 4);
-        const u32x4 w = {pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]), pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3])};
-        if (hd < nh) *(u32x4*)(obase16 + (size_t)hd * D + 32 * mt4 + 8 * pc) = w;
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {                               // head 8 k + lane / 8, d quad lane % 8
-        const int hd = 8 * k + (lane >> 3), pc = lane & 7;
-        if (hd < nh) *(f32x4*)(obase + (size_t)hd * D + 32 * mt4 + 4 * pc) = *(const f32x4*)(ob + hd * OPITCH + 4 * pc);
-      }
+    for (int k = 0; k < 4; ++k) {                                 // head 8 k + lane / 8, d quad lane % 8
+      const int hd = 8 * k + (lane >> 3), pc = lane & 7;
+      if (hd < nh) *(f32x4*)(obase + (size_t)hd * D + 32 * mt4 + 4 * pc) = *(const f32x4*)(ob + hd * OPITCH + 4 * pc);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");        // reads done before the next block's writes
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_fence();                                                 // reads done before the next block's writes
   }
 }
 
