@@ -469,6 +469,17 @@ hs_status swa_prepare(const hs_kv_cache* kv, const hs_attn_params* p, const void
   a.R = a.G; a.n_lists = kv->batch * ci.n_kv;
   a.scale_log2 = scale_log2(p);
   a.out = (float*)out; a.out_bf16 = od == HS_BF16; a.window = p->window;
+  // bf16 caches with windows the ring form holds: contiguous token ranges, a multiple of 8 tokens
+  // each, sized so the workgroups fill one round of the 256 CUs.  HS_SWA_RING=0 selects the
+  // per-group form, a value n >= 2 fixes n tokens (rounded up to a multiple of 8) per workgroup.
+  a.chunk = 0;
+  const int ring = env_int("HS_SWA_RING", 1);
+  if (kv->dtype == HS_BF16 && hs::swa_ring_fits(p->window) && ring != 0) {
+    const int64_t units = (int64_t)a.n_lists * ((a.G + 31) / 32);
+    const int64_t per_unit = std::max<int64_t>(1, (256 + units - 1) / units);
+    const int64_t tokens = ring >= 2 ? ring : (a.n_q + per_unit - 1) / per_unit;
+    a.chunk = (int)align_up((size_t)std::min<int64_t>(tokens, a.n_q), 8);
+  }
   return HS_OK;
 }
 

@@ -211,6 +211,9 @@ hipError_t launch_attn_wave(const AttnArgs& a, int kvt, hipStream_t st);
 // sparse layer, bf16 Q with a bf16 or FP8 cache, any G (blocks of 32 heads); chunk a multiple of 32
 hipError_t launch_attn_gather(const AttnArgs& a, int kvt, hipStream_t st);
 hipError_t launch_swa_attn(const AttnArgs& a, int kvt, hipStream_t st);
+// Whether the ring form of sliding-window attention (bf16 caches; a.chunk > 0 query tokens per
+// workgroup, a multiple of 8) holds the bands of a window this wide.
+bool swa_ring_fits(int window);
 hipError_t launch_attn_merge(const MergeArgs& m, hipStream_t st);
 // attn_rows: dense pass 1 for R > 32 query rows per list, bf16 or FP8 caches, bf16 MFMA;
 // nrg = query-row groups of 32 per workgroup (2, 4 or 8; rows beyond 32*nrg take more z blocks)
