@@ -92,15 +92,16 @@ def test_swa_bf16_output(kvtype, lens, n_kv, H, n_q, w):
           f"max-abs error beyond half a bf16 step {worst:.2e}", flush=True)
 
 
-@pytest.mark.parametrize("lens,H,n_q,w,ring", [
-    ([517, 250], 32, 200, 100, "24"),     # 3 groups of 8 per workgroup, a ragged last workgroup
-    ([300], 32, 300, 128, "64"),          # bands growing from 1 row; a partial last group
-    ([600], 40, 301, 154, "40"),          # widest window the ring holds; a partial second head block
-    ([90], 32, 90, 1, "16"),              # window 1
-    ([2600], 32, 2500, 128, "1"),         # the default split (16 tokens per workgroup here)
-    ([2600], 32, 2500, 128, "0"),         # the per-group form on a bf16 cache
+@pytest.mark.parametrize("lens,n_kv,H,n_q,w,ring", [
+    ([517, 250], 1, 32, 200, 100, "24"),  # 3 groups of 8 per workgroup, a ragged last workgroup
+    ([300], 1, 32, 300, 128, "64"),       # bands growing from 1 row; a partial last group
+    ([600], 1, 40, 301, 154, "40"),       # widest window the ring holds; a partial second head block
+    ([90], 1, 32, 90, 1, "16"),           # window 1
+    ([400, 333], 2, 64, 150, 128, "32"),  # two KV heads (32 query heads each), two sequences
+    ([2600], 1, 32, 2500, 128, "1"),      # the default split (16 tokens per workgroup here)
+    ([2600], 1, 32, 2500, 128, "0"),      # the per-group form on a bf16 cache
 ])
-def test_swa_ring_form(lens, H, n_q, w, ring, monkeypatch):
+def test_swa_ring_form(lens, n_kv, H, n_q, w, ring, monkeypatch):
     """bf16 caches: the ring form (tiles at absolute positions in an LDS ring, several 8-token
     groups per workgroup, HS_SWA_RING tokens per workgroup) and the per-group form (HS_SWA_RING=0)
     against the float64 oracle, every element written; the bf16 output equals the float32 one
@@ -108,8 +109,8 @@ def test_swa_ring_form(lens, H, n_q, w, ring, monkeypatch):
     from oracle import bf16
     from long_context_split_amd import hysparse as hs
     monkeypatch.setenv("HS_SWA_RING", ring)
-    banner(f"swa ring={ring} lens={lens} H={H} n_q={n_q} w={w}")
-    up = _case("bf16", lens, 1, H, n_q, seed=len(lens) * 1000 + w + H + 7)
+    banner(f"swa ring={ring} lens={lens} n_kv={n_kv} H={H} n_q={n_q} w={w}")
+    up = _case("bf16", lens, n_kv, H, n_q, seed=len(lens) * 1000 + w + H + 7)
     B, nq, Hq, _ = up.q_full.shape
     out = hs.swa_attn(up.kv, up.q_full, w,
                       out=torch.full((B, nq, Hq, 128), float("nan"), dtype=torch.float32, device="cuda"))
