@@ -8,7 +8,10 @@
 // sits at position p = L_b - n_q + i and attends to rows max(0, p - w + 1) .. p of its own cache,
 // the softmax taken over that band.
 //
-// One wave per query token and block of 32 query heads of one KV head, 4 waves (4 consecutive
+// Two forms share the tile step (swa_tile).  bf16 caches with windows up to 154 rows take the ring
+// form (swa_ring_kernel, further down): one workgroup per CU walks a range of tokens with its K/V
+// tiles held in an LDS ring.  E4M3 caches and wider windows take the per-group form described here:
+// one wave per query token and block of 32 query heads of one KV head, 4 waves (4 consecutive
 // tokens) per workgroup and two workgroups per CU (at most 256 VGPRs per wave), so one workgroup's
 // Q loads, first tiles and output stores overlap the other's tile work.  The 4 bands overlap
 // almost entirely, so the workgroup walks their union
